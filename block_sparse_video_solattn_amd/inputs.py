@@ -1,0 +1,168 @@
+"""Seeded synthetic inputs for the Sol-Attn workloads.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention method's arithmetic (no pooling, scoring, routing or softmax).  Both
+the HIP path (through the tests and the benchmark) and the CPU oracle receive
+the arrays it returns, so the two sides always see bit-identical inputs.
+
+Workload shapes follow the latent geometry the pages give for the two stages
+of the Sol-H3 pipeline:
+
+* draft stage: 672x384 canvas, 124 frames, 16x spatial compression
+  (page "NVIDIA 团队开源 Sol-H3 的 DGX Spark 版本", section "潜空间直传";
+  page "英伟达开源 Sol-H3", section 2.1 for the 16x / 32x VAE factors);
+* refine stage: 1344x768, 121 frames, 32x spatial / 8x temporal compression
+  (same pages, same sections).
+
+A packed sequence puts an always-exact prefix (text, conditioning video, audio)
+ahead of the target video tokens (page "英伟达开源 Sol-H3", section 2.2).  The
+prefix tokens here are i.i.d. normal stand-ins; the video tokens are a smooth
+3-D sinusoid field on the latent grid plus noise, so block scores vary the way
+spatially coherent latents make them vary.  Real latents need the model
+weights, which are not part of this operator.
+
+Random streams: every (batch, head) slice has its own PCG64 stream seeded with
+``SeedSequence([seed, b, h])``, so any subset of heads can be regenerated on
+its own.  Values are drawn in float64, cast to float32, and (for bf16
+workloads) rounded to the nearest bf16 value, ties to even.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+BLOCK = 64
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    D: int
+    dtype: str            # "f32" or "bf16"
+    prefix_len: int
+    taus: tuple           # tau values the workload is run at
+    grid: Optional[tuple]  # (T, Y, X) latent grid of the video tokens, None for iid
+    kind: str             # "iid_offset" or "field"
+
+    @property
+    def nb(self) -> int:
+        return (self.N + BLOCK - 1) // BLOCK
+
+
+# The five workloads.  Sizes: tokens = prefix + video; video = T*Y*X except
+# "small", whose grid is only partly filled (see video_positions()).
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 1, 1024, 64, "f32", 128, (1.0,), None, "iid_offset"),
+    "small": Workload("small", 1, 4, 8192, 128, "bf16", 256, (1.25,), (8, 24, 42), "field"),
+    "refine": Workload("refine", 1, 32, 256 + 16 * 24 * 42, 128, "bf16", 256,
+                       (1.0, 1.25, 1.5), (16, 24, 42), "field"),
+    "draft": Workload("draft", 1, 32, 512 + 32 * 24 * 42, 128, "bf16", 512,
+                      (), (32, 24, 42), "field"),
+    "long": Workload("long", 1, 32, 2048 + 46 * 24 * 42, 128, "bf16", 2048,
+                     (1.5,), (46, 24, 42), "field"),
+}
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bf16 value (ties to even), returned as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bf16-representable float32 array -> its uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def video_positions(n_video: int, grid: tuple) -> np.ndarray:
+    """(t, y, x) integer coordinates of the first n_video cells of the grid,
+    row-major (t slowest, x fastest)."""
+    T, Y, X = grid
+    assert n_video <= T * Y * X
+    idx = np.arange(n_video, dtype=np.int64)
+    return np.stack([idx // (Y * X), (idx // X) % Y, idx % X], axis=1)
+
+
+def _rng(seed: int, b: int, h: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, b, h])))
+
+
+def _head_iid_offset(rng, N, D):
+    out = []
+    nb = (N + BLOCK - 1) // BLOCK
+    for _ in range(3):  # Q, K, V
+        base = rng.standard_normal((N, D))
+        offs = rng.standard_normal((nb, D)) * 1.5
+        out.append(base + np.repeat(offs, BLOCK, axis=0)[:N])
+    return out
+
+
+def _head_field(rng, N, D, prefix_len, grid):
+    T, Y, X = grid
+    n_video = N - prefix_len
+    pos = video_positions(n_video, grid).astype(np.float64)
+    omega = rng.uniform(0.0, 2.0, size=(8, 3))          # cycles per axis extent
+    phi = rng.uniform(0.0, 2.0 * math.pi, size=8)
+    a_q = rng.standard_normal((8, D)) * math.sqrt(2.0 / 8.0)
+    a_k = rng.standard_normal((8, D)) * math.sqrt(2.0 / 8.0)
+    pre = [rng.standard_normal((prefix_len, D)) for _ in range(3)]
+    arg = 2.0 * math.pi * (pos[:, 0:1] * omega[None, :, 0] / T
+                           + pos[:, 1:2] * omega[None, :, 1] / Y
+                           + pos[:, 2:3] * omega[None, :, 2] / X) + phi[None, :]
+    basis = np.sin(arg)                                    # [n_video, 8]
+    q_vid = basis @ a_q + rng.standard_normal((n_video, D)) * 0.5
+    k_vid = basis @ a_k + rng.standard_normal((n_video, D)) * 0.5
+    v_vid = rng.standard_normal((n_video, D))
+    return [np.concatenate([pre[0], q_vid]), np.concatenate([pre[1], k_vid]),
+            np.concatenate([pre[2], v_vid])]
+
+
+def make_inputs(w: Workload, seed: int, heads: Optional[Sequence[int]] = None,
+                const_key_block: Optional[int] = None):
+    """Return (q, k, v) as float32 arrays [B, len(heads), N, D].
+
+    For bf16 workloads every value is already a bf16 value.  ``heads`` selects
+    a subset (default all); the values of a head do not depend on which other
+    heads are generated.  ``const_key_block`` makes every key and value row of
+    that key block equal to the block's first row (the "constant block" case).
+    """
+    heads = list(range(w.H)) if heads is None else list(heads)
+    shape = (w.B, len(heads), w.N, w.D)
+    q = np.empty(shape, np.float32)
+    k = np.empty(shape, np.float32)
+    v = np.empty(shape, np.float32)
+    for b in range(w.B):
+        for hi, h in enumerate(heads):
+            rng = _rng(seed, b, h)
+            if w.kind == "iid_offset":
+                qq, kk, vv = _head_iid_offset(rng, w.N, w.D)
+            else:
+                qq, kk, vv = _head_field(rng, w.N, w.D, w.prefix_len, w.grid)
+            q[b, hi], k[b, hi], v[b, hi] = qq, kk, vv
+    if const_key_block is not None:
+        j = const_key_block
+        lo, hi_ = j * BLOCK, min(w.N, (j + 1) * BLOCK)
+        k[:, :, lo:hi_] = k[:, :, lo:lo + 1]
+        v[:, :, lo:hi_] = v[:, :, lo:lo + 1]
+    if w.dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    return q, k, v
+
+
+def custom(B, H, N, D, dtype="bf16", prefix_len=0, seed=0, kind="iid_offset",
+           grid=None) -> tuple:
+    """Inputs for an arbitrary shape (edge-case tests)."""
+    if kind == "field" and grid is None:
+        n_video = N - prefix_len
+        grid = (1, 1, max(1, n_video))
+    w = Workload("custom", B, H, N, D, dtype, prefix_len, (), grid, kind)
+    return make_inputs(w, seed)
