@@ -1,0 +1,214 @@
+"""Sol-Attn forward benchmark on one MI355X.
+
+A step is one full forward call (pooling kernel + fused routing/attention
+kernel) over the refine-stage workload: B=1, H=32, N = 256 text + 16128 video
+tokens (16x24x42 latent of a 1344x768, 121-frame clip), d=128, bf16, prefix
+256, tau=1.25, synthetic field inputs resident in HBM.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--tau T] [--no-cpu] [--no-extra]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/call + dense-equiv TFLOP/s and % bf16 MFMA peak on kept tiles, N=16128 refine"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0
+SEED = 3000
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kept_flops(mask, N, d):
+    """4*d*sum over (h, i, kept j) rows_i * n_j, and the same for pooled
+    (skipped) blocks counted once each."""
+    import numpy as np
+    nb = mask.shape[-1]
+    n = np.full(nb, 64, dtype=np.float64)
+    n[-1] = N - 64 * (nb - 1)
+    rows = n  # query rows of block i
+    kept = (mask * n[None, None, None, :]).sum(-1)          # [B,H,nb] keys kept
+    skipped = (~mask).sum(-1)                                # pooled terms
+    fk = 4.0 * d * float((kept * rows[None, None, :]).sum())
+    fp = 4.0 * d * float((skipped * rows[None, None, :]).sum())
+    return fk, fp
+
+
+def time_calls(fn, n, stream):
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record(stream)
+    for i in range(n):
+        fn()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+
+
+def cpu_baseline(q, k, v, w, tau, budget_s=15.0):
+    """The fp64 oracle (as it stands) on whole heads until ~budget_s of work,
+    scaled to one call over all heads."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    t0 = time.time()
+    heads = 0
+    for h in range(w.H):
+        oracle.head(q[0, h], k[0, h], v[0, h], w.prefix_len, tau, threads=threads)
+        heads += 1
+        if time.time() - t0 > budget_s:
+            break
+    dt = time.time() - t0
+    return {"value": round(dt / heads * w.H * 1000.0, 1), "unit": "ms/call", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d heads of the same refine call (sparse, tau=%g, all query blocks), "
+                      "scaled by %d/%d" % (heads, w.H, tau, w.H, heads)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--tau", type=float, default=1.25)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip dense / tau sweep / setup timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this operator is measured at one GPU's share; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_video_solattn_amd as sa
+    from block_sparse_video_solattn_amd import inputs
+
+    w = inputs.WORKLOADS["refine"]
+    B, H, N, d = w.B, w.H, w.N, w.D
+    tau = args.tau
+    log("generating refine inputs (B=%d H=%d N=%d d=%d)" % (B, H, N, d))
+    q, k, v = inputs.make_inputs(w, SEED)
+    dev = [torch.from_numpy(x).to("cuda").to(torch.bfloat16).contiguous() for x in (q, k, v)]
+    qd, kd, vd = dev
+    out = torch.empty_like(qd)
+    ws = torch.empty(sa.solattn_workspace_bytes(B, H, N, d, sa.BF16), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    # routing of this call (outside the timed region) for the FLOP accounting
+    words, _, _ = sa.solattn_route(qd, kd, vd, w.prefix_len, tau, want_scores=False)
+    torch.cuda.synchronize()
+    mask = sa.unpack_mask(words, w.nb)
+    fk, fp = kept_flops(mask, N, d)
+    pb = (w.prefix_len + 63) // 64
+    video_skip = float(1.0 - mask[..., pb:].mean())
+    log("tau %.3g: kept blocks/row %.1f of %d, video skip %.4f" % (tau, mask.sum(-1).mean(), w.nb,
+                                                                   video_skip))
+
+    def step():
+        sa.solattn_prepare_ws(qd, kd, vd, "sparse", ws)
+        sa.solattn_attend_ws(qd, kd, vd, out, w.prefix_len, tau, "sparse", ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-kernel HIP events on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        sa.solattn_prepare_ws(qd, kd, vd, "sparse", ws)
+        ev[i][1].record(stream)
+        sa.solattn_attend_ws(qd, kd, vd, out, w.prefix_len, tau, "sparse", ws)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    pool_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    call_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = wall_ms  # wall clock over the K steps, synchronised on both sides
+
+    dense_flops = 4.0 * B * H * N * N * d
+    attn_tflops = fk / (attn_ms * 1e-3) / 1e12
+    pool_read = 3.0 * B * H * N * d * 2
+    res = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 4),
+        "unit": "ms/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "refine: 1344x768 121 frames -> 16x24x42 latent, 256 text + 16128 "
+                               "video tokens", "B": B, "H": H, "N": N, "d": d,
+                   "prefix_len": w.prefix_len, "tau": tau},
+        "dense_equiv_tflops": round(dense_flops / (ms_per_step * 1e-3) / 1e12, 1),
+        "kept_tile_mfma_frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "kept_tile_mfma_frac_with_pooled": round((fk + fp) / (attn_ms * 1e-3) / 1e12
+                                                 / PEAK_BF16_TFLOPS, 4),
+        "gpu_event_ms_per_call": round(call_ms, 4),
+        "pool_ms": round(pool_ms, 4),
+        "attn_ms": round(attn_ms, 4),
+        "pool_read_GBps": round(pool_read / (pool_ms * 1e-3) / 1e9, 1),
+        "video_block_sparsity": round(video_skip, 4),
+        "kept_tile_tflop": round(fk / 1e12, 4),
+        "pooled_tflop": round(fp / 1e12, 5),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_bf16_kernel<128>"},
+    }
+
+    if not args.no_extra:
+        # in-run dense reference (tau = -inf semantics, every tile exact)
+        def dense():
+            sa.solattn_forward_ws(qd, kd, vd, out, w.prefix_len, 0.0, "dense", ws)
+        for _ in range(3):
+            dense()
+        dms = float(np.median(time_calls(dense, 10, stream)))
+        res["dense_ms"] = round(dms, 3)
+        res["speedup_vs_dense"] = round(dms / ms_per_step, 2)
+        sweep = {}
+        for t in w.taus:
+            def sp(t=t):
+                sa.solattn_forward_ws(qd, kd, vd, out, w.prefix_len, t, "sparse", ws)
+            sp()
+            wd, _, _ = sa.solattn_route(qd, kd, vd, w.prefix_len, t, want_scores=False)
+            torch.cuda.synchronize()
+            m = sa.unpack_mask(wd, w.nb)
+            tms = float(np.median(time_calls(sp, 20, stream)))
+            sweep[str(t)] = {"ms": round(tms, 4), "video_sparsity": round(float(1 - m[..., pb:].mean()), 4),
+                             "speedup_vs_dense": round(dms / tms, 2)}
+        res["tau_sweep"] = sweep
+        # routing setup (pooling + scoring/threshold, no attention)
+        mw = torch.zeros((B, H, w.nb, (w.nb + 31) // 32), dtype=torch.int32, device="cuda")
+        th = torch.zeros((B, H, w.nb), dtype=torch.float32, device="cuda")
+
+        def setup():
+            sa.solattn_route(qd, kd, vd, w.prefix_len, tau, want_scores=False, mask=mw, thr=th)
+        setup()
+        res["setup_ms"] = round(float(np.median(time_calls(setup, 20, stream))), 4)
+
+    if not args.no_cpu:
+        log("timing the CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(q, k, v, w, tau)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

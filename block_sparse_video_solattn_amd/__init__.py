@@ -1,0 +1,20 @@
+"""Sol-Attn block-sparse video attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in the HIP library libsolattn.so (C ABI in include/solattn.h);
+this package re-exports its thin Python binding on first use.  Using it without
+the built library raises ImportError: there is no CPU fallback.  The input
+generators in ``.inputs`` need no library.
+"""
+_BINDING_NAMES = (
+    "BF16", "DENSE", "EXPORTS", "F32", "SPARSE", "SolAttnError", "solattn_attend_ws",
+    "solattn_forward", "solattn_forward_debug", "solattn_forward_ws", "solattn_last_error",
+    "solattn_pool", "solattn_prepare_ws", "solattn_route", "solattn_strerror",
+    "solattn_version", "solattn_workspace_bytes", "unpack_mask", "raw_call",
+)
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import _binding
+        return getattr(_binding, name)
+    raise AttributeError(name)

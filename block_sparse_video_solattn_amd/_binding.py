@@ -1,0 +1,235 @@
+"""Thin ctypes binding over libsolattn.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  Tensors are torch device tensors (used for device
+memory and streams); shapes are read from q, which must be contiguous
+[B, H, N, d].  A missing library raises at import time; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsolattn.so")
+
+OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
+DENSE, SPARSE = 0, 1
+F32, BF16 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libsolattn.so is not built (expected at %s); run "
+        "`python -m block_sparse_video_solattn_amd.build`" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "solattn_forward": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P], _I),
+    "solattn_workspace_bytes": ([_I64, _I64, _I64, _I64, _I], _SZ),
+    "solattn_forward_ws": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P, _SZ, _P], _I),
+    "solattn_prepare_ws": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I, _I, _P, _SZ, _P], _I),
+    "solattn_attend_ws": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P, _SZ, _P], _I),
+    "solattn_forward_debug": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P, _P, _P, _P], _I),
+    "solattn_pool": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P], _I),
+    "solattn_route": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _P, _P, _P, _P], _I),
+    "solattn_strerror": ([_I], ctypes.c_char_p),
+    "solattn_last_error": ([], ctypes.c_char_p),
+    "solattn_version": ([], ctypes.c_char_p),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTS = tuple(_SIGS)
+
+
+class SolAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("solattn error %d (%s): %s" % (code, solattn_strerror(code), msg))
+        self.code = code
+
+
+def solattn_strerror(code: int) -> str:
+    return _lib.solattn_strerror(int(code)).decode()
+
+
+def solattn_last_error() -> str:
+    return _lib.solattn_last_error().decode()
+
+
+def solattn_version() -> str:
+    return _lib.solattn_version().decode()
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise SolAttnError(rc, solattn_last_error())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("q/k/v must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _mode_code(mode) -> int:
+    if isinstance(mode, str):
+        return {"dense": DENSE, "sparse": SPARSE}[mode]
+    return int(mode)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    for t in (q,):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return tuple(int(x) for x in q.shape)
+
+
+def _check_like(q, *ts):
+    for t in ts:
+        if t is None:
+            continue
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("q, k, v, out must share shape, dtype, device and be contiguous")
+
+
+def solattn_workspace_bytes(B: int, H: int, N: int, d: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(_lib.solattn_workspace_bytes(B, H, N, d, code))
+
+
+def solattn_forward(q, k, v, out=None, prefix_len: int = 0, tau: float = 1.0, mode="sparse",
+                    stream=None):
+    """out = Sol-Attn(q, k, v); returns out (allocated when not given)."""
+    B, H, N, d = _shape(q)
+    if out is None:
+        out = q.new_empty(q.shape)
+    _check_like(q, k, v, out)
+    _check(_lib.solattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, prefix_len,
+                                float(tau), _mode_code(mode), _dtype_code(q), _stream(stream)))
+    return out
+
+
+def solattn_forward_ws(q, k, v, out, prefix_len, tau, mode, ws, stream=None):
+    B, H, N, d = _shape(q)
+    _check_like(q, k, v, out)
+    _check(_lib.solattn_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, prefix_len,
+                                   float(tau), _mode_code(mode), _dtype_code(q), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def solattn_prepare_ws(q, k, v, mode, ws, stream=None):
+    B, H, N, d = _shape(q)
+    _check_like(q, k, v)
+    _check(_lib.solattn_prepare_ws(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, _mode_code(mode),
+                                   _dtype_code(q), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)))
+
+
+def solattn_attend_ws(q, k, v, out, prefix_len, tau, mode, ws, stream=None):
+    B, H, N, d = _shape(q)
+    _check_like(q, k, v, out)
+    _check(_lib.solattn_attend_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, prefix_len,
+                                  float(tau), _mode_code(mode), _dtype_code(q), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def solattn_forward_debug(q, k, v, out=None, prefix_len: int = 0, tau: float = 1.0,
+                          mode="sparse", stream=None, want_scores: bool = True):
+    """Forward plus the routing exports.  Returns (out, mask_words, scores, thr)."""
+    import torch
+    B, H, N, d = _shape(q)
+    nb = (N + 63) // 64
+    if out is None:
+        out = q.new_empty(q.shape)
+    _check_like(q, k, v, out)
+    mask = torch.zeros((B, H, nb, (nb + 31) // 32), dtype=torch.int32, device=q.device)
+    scores = (torch.full((B, H, nb, nb), float("nan"), dtype=torch.float32, device=q.device)
+              if want_scores else None)
+    thr = torch.full((B, H, nb), float("nan"), dtype=torch.float32, device=q.device)
+    _check(_lib.solattn_forward_debug(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d,
+                                      prefix_len, float(tau), _mode_code(mode), _dtype_code(q),
+                                      _ptr(mask), _ptr(scores), _ptr(thr), _stream(stream)))
+    return out, mask, scores, thr
+
+
+def solattn_pool(q, k, v, stream=None):
+    """Block means (fp32 [B, H, Nb, d]) of q, k, v."""
+    import torch
+    B, H, N, d = _shape(q)
+    _check_like(q, k, v)
+    nb = (N + 63) // 64
+    outs = [torch.empty((B, H, nb, d), dtype=torch.float32, device=q.device) for _ in range(3)]
+    _check(_lib.solattn_pool(_ptr(q), _ptr(k), _ptr(v), _ptr(outs[0]), _ptr(outs[1]),
+                             _ptr(outs[2]), B, H, N, d, _dtype_code(q), _stream(stream)))
+    return tuple(outs)
+
+
+def solattn_route(q, k, v, prefix_len: int, tau: float, stream=None, want_scores: bool = True,
+                  mask=None, scores=None, thr=None):
+    """Pooling + routing only.  Returns (mask_words, scores, thr)."""
+    import torch
+    B, H, N, d = _shape(q)
+    _check_like(q, k, v)
+    nb = (N + 63) // 64
+    if mask is None:
+        mask = torch.zeros((B, H, nb, (nb + 31) // 32), dtype=torch.int32, device=q.device)
+    if scores is None and want_scores:
+        scores = torch.full((B, H, nb, nb), float("nan"), dtype=torch.float32, device=q.device)
+    if thr is None:
+        thr = torch.full((B, H, nb), float("nan"), dtype=torch.float32, device=q.device)
+    _check(_lib.solattn_route(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, prefix_len, float(tau),
+                              _dtype_code(q), _ptr(mask), _ptr(scores), _ptr(thr), _stream(stream)))
+    return mask, scores, thr
+
+
+def raw_call(name: str, *args) -> int:
+    """Call an exported C function with raw integer/float arguments (for
+    argument-validation tests)."""
+    return getattr(_lib, name)(*args)
+
+
+def unpack_mask(words, nb: int):
+    """[..., ceil(nb/32)] int32 words -> [..., nb] bool keep mask (host numpy)."""
+    import numpy as np
+    w = words.cpu().numpy().astype(np.uint32) if hasattr(words, "cpu") else np.asarray(words, np.uint32)
+    bits = (w[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1
+    return bits.reshape(w.shape[:-1] + (-1,))[..., :nb].astype(bool)
+
+
+def isinf_tau(tau: float) -> bool:
+    return math.isinf(tau)

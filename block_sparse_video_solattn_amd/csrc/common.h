@@ -1,0 +1,71 @@
+// Shared device-side definitions of the Sol-Attn HIP library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace solattn {
+
+constexpr int kBlock = 64;        // routing block: 64 tokens on the query and the key side
+constexpr int kMaxNb = 4096;      // largest number of 64-token blocks per sequence (N <= 262144)
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+// Number of 64-token blocks of an N-token sequence, and the pooled-key count
+// padded to whole 64-wide tiles.
+__host__ __device__ inline int64_t num_blocks(int64_t N) { return (N + kBlock - 1) / kBlock; }
+__host__ __device__ inline int64_t padded_blocks(int64_t nb) { return (nb + 63) / 64 * 64; }
+
+// Element offset of (mt, s, lane, e) inside one 64-key value tile laid out in
+// the A-operand order of v_mfma_f32_32x32x16_bf16 for O^T = V^T P^T:
+// 16-byte group (mt*4 + s)*64 + lane holds V[key(s, lane/32, e)][32*mt + lane%32]
+// for e = 0..7.  The key order inside each 16-key step matches the row order
+// of the 32x32 MFMA accumulator (rows 4h..4h+3 and 4h+8..4h+11 of each
+// 16-row half belong to lane half h), so P^T needs no shuffle.
+__host__ __device__ inline int vtile_offset(int mt, int s, int lane, int e) {
+    return ((mt * 4 + s) * 64 + lane) * 8 + e;
+}
+__host__ __device__ inline int vtile_key(int s, int half, int e) {
+    return 16 * s + 4 * half + (e < 4 ? e : e + 4);
+}
+// Inverse: (s, half, e) of key kk (0..63) inside a tile.
+__host__ __device__ inline void vtile_slot(int kk, int* s, int* half, int* e) {
+    int r = kk & 15;
+    *s = kk >> 4;
+    *half = (r >> 2) & 1;
+    *e = (r & 3) + 4 * (r >> 3);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs).
+__device__ inline bf16 to_bf16(float x) { return (bf16)x; }
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__device__ inline float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+// Workgroup index -> work item, so that consecutive work items (query blocks
+// of one head) land on the same XCD.  The dispatcher deals workgroups to the
+// 8 XCDs round robin; XCD x receives ids x, x+8, ... and is given the
+// contiguous range of work items starting at x*(T/8) + min(x, T%8).
+__device__ inline int64_t xcd_remap(int64_t g, int64_t T) {
+    int64_t x = g % 8, r = g / 8;
+    int64_t q = T / 8, m = T % 8;
+    return x * q + (x < m ? x : m) + r;
+}
+
+}  // namespace solattn

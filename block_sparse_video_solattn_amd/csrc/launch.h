@@ -1,0 +1,91 @@
+// Internal host <-> kernel interface of the Sol-Attn library: workspace layout,
+// kernel argument blocks and launch functions.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace solattn {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+enum Mode { kDense = 0, kSparse = 1 };
+
+// Workspace regions (byte offsets, each 256-byte aligned).  BH = B*H,
+// Nb = ceil(N/64), Nbp = Nb rounded up to a multiple of 64.
+//   qbar, kbar, vbar  fp32 [BH][Nb][d]     block means
+//   kbarT             fp32 [BH][d][Nbp]    block means of K, transposed for the
+//                                          coalesced score pass; zero padded
+//   kbar16            bf16 [BH][Nbp][d]    pooled keys, MFMA operand (bf16 only)
+//   vbarP             bf16 [BH][Nbp/64][d*64] pooled values, MFMA operand order
+//   vP                bf16 [BH][Nb][d*64]  value tiles, MFMA operand order
+struct WsLayout {
+    size_t qbar, kbar, vbar, kbarT, kbar16, vbarP, vP, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+inline WsLayout ws_layout(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    const int64_t BH = B * H, Nb = (N + 63) / 64, Nbp = (Nb + 63) / 64 * 64;
+    WsLayout w;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    w.qbar = take(sizeof(float) * BH * Nb * d);
+    w.kbar = take(sizeof(float) * BH * Nb * d);
+    w.vbar = take(sizeof(float) * BH * Nb * d);
+    w.kbarT = take(sizeof(float) * BH * d * Nbp);
+    if (dtype == kBF16) {
+        w.kbar16 = take(2 * BH * Nbp * d);
+        w.vbarP = take(2 * BH * Nbp * d);
+        w.vP = take(2 * BH * Nb * 64 * d);
+    } else {
+        w.kbar16 = w.vbarP = w.vP = 0;
+    }
+    w.total = off;
+    return w;
+}
+
+struct PoolArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    float* qbar;
+    float* kbar;
+    float* vbar;
+    float* kbarT;
+    void* kbar16;
+    void* vbarP;
+    void* vP;
+    int64_t N, Nb, Nbp;
+    int d, dtype;
+    int pooled;   // compute block means (sparse mode)
+    int pack_v;   // write the operand-ordered value tiles (bf16)
+};
+
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* vP;       // bf16: value tiles; f32: unused
+    const void* v;        // f32 path reads V directly
+    const void* kbar16;
+    const void* vbarP;
+    const float* kbar;    // f32 path pooled operands
+    const float* vbar;
+    const float* qbar;
+    const float* kbarT;
+    void* out;
+    uint32_t* mask_out;   // debug exports (NULL in production)
+    float* score_out;
+    float* thr_out;
+    int64_t BH, N, Nb, Nbp;
+    int64_t Pb;
+    float tau;
+    int d, dtype, mode;
+    int route_only;       // stop after routing (setup timing / export)
+};
+
+hipError_t launch_pool(const PoolArgs& a, int64_t BH, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+
+}  // namespace solattn

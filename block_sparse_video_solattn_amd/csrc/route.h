@@ -1,0 +1,119 @@
+// Step 2 of Sol-Attn: block scores, the query-adaptive threshold and the keep
+// mask of one query block, computed by one wavefront into LDS.
+//
+// The rule (page "MiniMax 官宣 NVIDIA Sol 团队 H3 加速:5 秒视频 1.653 秒生成并
+// 开源", section "提速来自流水线每一段的叠加"; page "NVIDIA 团队开源 Sol-H3 的
+// DGX Spark 版本", section "119.68 GiB 的内存池"): every query block scores all
+// key blocks with a lightweight score and keeps those that clear its own
+// threshold, mean + tau * standard deviation of its score row.  Key blocks of
+// the packed prefix are always kept (page "英伟达开源 Sol-H3", section 2.2).
+// Readings taken where the pages are silent: the score is the pooled-mean dot
+// product scaled by 1/sqrt(d); the standard deviation is the population one
+// over all Nb key blocks; a score equal to the threshold is kept; tau = -inf
+// keeps all, tau = +inf keeps only the prefix, sigma = 0 uses the mean.
+//
+// Nothing of the routing reaches device memory except through the debug
+// exports: the mask lives as ballot words, the kept-block list and the
+// pooled-term biases in LDS.
+#pragma once
+
+#include "common.h"
+#include "launch.h"
+
+namespace solattn {
+
+struct RouteResult {
+    int n_kept;          // kept key blocks, listed ascending in klist[0..n_kept)
+    uint64_t tile_mask;  // bit T set when pooled tile T (key blocks 64T..64T+63)
+                         // holds at least one skipped block
+};
+
+// One wavefront (all 64 lanes of the workgroup).  On return:
+//   klist[0..n_kept)  kept key-block indices (ascending)
+//   srow[0..Nbp)      log2(n_j) for skipped blocks, -inf for kept and padding
+//                     (the per-column bias of the pooled tiles, log2 units)
+template <int D>
+__device__ inline RouteResult route_query_block(const AttnArgs& a, int64_t bh, int64_t i,
+                                                float* srow, uint16_t* klist) {
+    const int lane = threadIdx.x & 63;
+    const int64_t Nb = a.Nb, Nbp = a.Nbp;
+    const float scale = 1.0f / sqrtf((float)D);
+
+    // scores s_ij = qbar_i . kbar_j / sqrt(d); kbar is stored transposed so each
+    // load instruction reads 1 KiB of consecutive key blocks.
+    const float* __restrict__ qb = a.qbar + (bh * Nb + i) * D;
+    const float* __restrict__ kt = a.kbarT + bh * D * Nbp;
+    for (int64_t j0 = 4 * lane; j0 < Nbp; j0 += 256) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
+        for (int d = 0; d < D; ++d) {
+            const float qv = qb[d];
+            const f32x4 kv = *reinterpret_cast<const f32x4*>(kt + (int64_t)d * Nbp + j0);
+            acc += qv * kv;
+        }
+        *reinterpret_cast<f32x4*>(srow + j0) = acc * scale;
+    }
+    __syncthreads();
+
+    // row statistics, two passes (mean, then squared deviations)
+    float part = 0.f;
+    for (int64_t j = lane; j < Nb; j += 64) part += srow[j];
+    const float mu = wave_sum(part) / (float)Nb;
+    part = 0.f;
+    for (int64_t j = lane; j < Nb; j += 64) {
+        const float t = srow[j] - mu;
+        part += t * t;
+    }
+    const float sigma = sqrtf(wave_sum(part) / (float)Nb);
+    float thr;
+    if (__builtin_isinf(a.tau))
+        thr = a.tau;
+    else if (sigma == 0.f)
+        thr = mu;
+    else
+        thr = mu + a.tau * sigma;
+
+    // keep bits, kept list, pooled-tile flags, pooled biases
+    int n_kept = 0;
+    uint64_t tile_mask = 0;
+    const int64_t W = (Nb + 31) / 32;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int64_t j0 = 0; j0 < Nbp; j0 += 64) {
+        const int64_t j = j0 + lane;
+        const bool valid = j < Nb;
+        const float s = srow[j];
+        const bool keep = valid && (j < a.Pb || s >= thr);
+        const bool skip = valid && !keep;
+        const uint64_t kb = __ballot(keep);
+        const uint64_t sb = __ballot(skip);
+        if (a.score_out && valid) a.score_out[(bh * Nb + i) * Nb + j] = s;
+        if (a.mask_out) {
+            const int64_t w0 = j0 / 32;
+            if (lane == 0 && w0 < W) a.mask_out[(bh * Nb + i) * W + w0] = (uint32_t)kb;
+            if (lane == 1 && w0 + 1 < W) a.mask_out[(bh * Nb + i) * W + w0 + 1] = (uint32_t)(kb >> 32);
+        }
+        if (keep) klist[n_kept + __popcll(kb & lt)] = (uint16_t)j;
+        n_kept += __popcll(kb);
+        if (sb) tile_mask |= 1ull << (j0 / 64);
+        const int nj = (int)((j + 1) * 64 <= a.N ? 64 : a.N - j * 64);
+        srow[j] = skip ? log2f((float)nj) : -__builtin_inff();
+    }
+    if (a.thr_out && lane == 0) a.thr_out[bh * Nb + i] = thr;
+    __syncthreads();
+    return RouteResult{n_kept, tile_mask};
+}
+
+// Dense mode exports: every bit set, threshold -inf.
+__device__ inline void export_dense_route(const AttnArgs& a, int64_t bh, int64_t i) {
+    const int lane = threadIdx.x & 63;
+    const int64_t Nb = a.Nb, W = (Nb + 31) / 32;
+    if (a.mask_out) {
+        for (int64_t w = lane; w < W; w += 64) {
+            const int64_t bits = Nb - 32 * w;
+            a.mask_out[(bh * Nb + i) * W + w] = bits >= 32 ? 0xffffffffu : ((1u << bits) - 1u);
+        }
+    }
+    if (a.thr_out && lane == 0) a.thr_out[bh * Nb + i] = -__builtin_inff();
+}
+
+}  // namespace solattn

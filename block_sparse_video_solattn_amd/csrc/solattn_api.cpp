@@ -1,0 +1,304 @@
+// Host side of the Sol-Attn C ABI: argument checks, the per-device workspace
+// cache, and the launch sequence (pool, then fused route + attention).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/solattn.h"
+#include "launch.h"
+
+using namespace solattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(SOLATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxN = 64LL * 4096;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// Every check happens here, on the host, before any device call.
+int validate(const void* q, const void* k, const void* v, const void* out, bool need_out,
+             int64_t B, int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau, int mode,
+             int dtype) {
+    g_last_error.clear();
+    if (!q || !k || !v) return fail(SOLATTN_EINVAL, "q, k and v must be non-NULL");
+    if (need_out && !out) return fail(SOLATTN_EINVAL, "out must be non-NULL");
+    if (B < 1 || H < 1 || N < 1)
+        return fail(SOLATTN_EINVAL, "B, H, N must be >= 1 (got %lld, %lld, %lld)", (long long)B,
+                    (long long)H, (long long)N);
+    if (d != 64 && d != 128) return fail(SOLATTN_EINVAL, "d must be 64 or 128 (got %lld)", (long long)d);
+    if (prefix_len < 0 || prefix_len > N)
+        return fail(SOLATTN_EINVAL, "prefix_len must lie in [0, N] (got %lld)", (long long)prefix_len);
+    if (std::isnan(tau)) return fail(SOLATTN_EINVAL, "tau must not be NaN");
+    if (mode != SOLATTN_DENSE && mode != SOLATTN_SPARSE)
+        return fail(SOLATTN_EINVAL, "unknown mode %d", mode);
+    if (dtype != SOLATTN_F32 && dtype != SOLATTN_BF16)
+        return fail(SOLATTN_EINVAL, "unknown dtype %d", dtype);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (out && !aligned16(out)))
+        return fail(SOLATTN_EINVAL, "tensor pointers must be 16-byte aligned");
+    if (N > kMaxN)
+        return fail(SOLATTN_EUNSUPPORTED, "N = %lld exceeds the supported maximum %lld",
+                    (long long)N, (long long)kMaxN);
+    if (B > (int64_t(1) << 40) / H || B * H > (int64_t(1) << 31) / ((N + 63) / 64))
+        return fail(SOLATTN_EUNSUPPORTED, "B*H*ceil(N/64) exceeds 2^31 workgroups");
+    if (out) {
+        const size_t bytes = (size_t)B * H * N * d * (dtype == SOLATTN_BF16 ? 2 : 4);
+        if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+            overlaps(out, bytes, v, bytes))
+            return fail(SOLATTN_EINVAL, "out must not overlap q, k or v");
+    }
+    return SOLATTN_OK;
+}
+
+struct DeviceWs {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::vector<DeviceWs> g_ws;
+
+// Internal workspace of the current device, grown on demand.  Growing
+// synchronises the device first so no launch still reads the old buffer.
+int internal_ws(size_t need, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+    DeviceWs& w = g_ws[dev];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+            e = hipFree(w.ptr);
+            if (e != hipSuccess) return hip_fail(e, "hipFree");
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        e = hipMalloc(&w.ptr, need);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            (void)hipGetLastError();
+            return fail(SOLATTN_ENOMEM, "workspace allocation of %zu bytes failed: %s", need,
+                        hipGetErrorString(e));
+        }
+        w.bytes = need;
+    }
+    *out = w.ptr;
+    return SOLATTN_OK;
+}
+
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+int run_prepare(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t N,
+                int64_t d, int mode, int dtype, void* ws, hipStream_t s, bool pack_v) {
+    const WsLayout L = ws_layout(B, H, N, d, dtype);
+    PoolArgs p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.qbar = reinterpret_cast<float*>(at(ws, L.qbar));
+    p.kbar = reinterpret_cast<float*>(at(ws, L.kbar));
+    p.vbar = reinterpret_cast<float*>(at(ws, L.vbar));
+    p.kbarT = reinterpret_cast<float*>(at(ws, L.kbarT));
+    p.kbar16 = dtype == kBF16 ? at(ws, L.kbar16) : nullptr;
+    p.vbarP = dtype == kBF16 ? at(ws, L.vbarP) : nullptr;
+    p.vP = dtype == kBF16 ? at(ws, L.vP) : nullptr;
+    p.N = N;
+    p.Nb = (N + 63) / 64;
+    p.Nbp = (p.Nb + 63) / 64 * 64;
+    p.d = (int)d;
+    p.dtype = dtype;
+    p.pooled = mode == SOLATTN_SPARSE;
+    p.pack_v = pack_v && dtype == kBF16;
+    if (!p.pooled && !p.pack_v) return SOLATTN_OK;  // fp32 dense: nothing to prepare
+    hipError_t e = launch_pool(p, B * H, s);
+    if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
+    return SOLATTN_OK;
+}
+
+int run_attend(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
+               int64_t N, int64_t d, int64_t prefix_len, float tau, int mode, int dtype, void* ws,
+               hipStream_t s, uint32_t* mask_out, float* score_out, float* thr_out,
+               int route_only) {
+    const WsLayout L = ws_layout(B, H, N, d, dtype);
+    AttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.vP = dtype == kBF16 ? at(ws, L.vP) : nullptr;
+    a.kbar16 = dtype == kBF16 ? at(ws, L.kbar16) : nullptr;
+    a.vbarP = dtype == kBF16 ? at(ws, L.vbarP) : nullptr;
+    a.kbar = reinterpret_cast<const float*>(at(ws, L.kbar));
+    a.vbar = reinterpret_cast<const float*>(at(ws, L.vbar));
+    a.qbar = reinterpret_cast<const float*>(at(ws, L.qbar));
+    a.kbarT = reinterpret_cast<const float*>(at(ws, L.kbarT));
+    a.out = out;
+    a.mask_out = mask_out;
+    a.score_out = mode == SOLATTN_SPARSE ? score_out : nullptr;
+    a.thr_out = thr_out;
+    a.BH = B * H;
+    a.N = N;
+    a.Nb = (N + 63) / 64;
+    a.Nbp = (a.Nb + 63) / 64 * 64;
+    a.Pb = (prefix_len + 63) / 64;
+    a.tau = tau;
+    a.d = (int)d;
+    a.dtype = dtype;
+    a.mode = mode;
+    a.route_only = route_only;
+    hipError_t e = dtype == kBF16 ? launch_attn_bf16(a, s) : launch_attn_f32(a, s);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    return SOLATTN_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    const size_t need = ws_layout(B, H, N, d, dtype).total;
+    if (!ws) return fail(SOLATTN_EINVAL, "ws must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(SOLATTN_EINVAL, "ws must be 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(SOLATTN_EINVAL, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    return SOLATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t solattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128) || (dtype != 0 && dtype != 1)) return 0;
+    return ws_layout(B, H, N, d, dtype).total;
+}
+
+int solattn_forward_ws(const void* q, const void* k, const void* v, void* out, int64_t B,
+                       int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau, int mode,
+                       int dtype, void* ws, size_t ws_bytes, void* stream) {
+    int rc = validate(q, k, v, out, true, B, H, N, d, prefix_len, tau, mode, dtype);
+    if (rc) return rc;
+    if ((rc = check_ws(ws, ws_bytes, B, H, N, d, dtype))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = run_prepare(q, k, v, B, H, N, d, mode, dtype, ws, s, true))) return rc;
+    return run_attend(q, k, v, out, B, H, N, d, prefix_len, tau, mode, dtype, ws, s, nullptr,
+                      nullptr, nullptr, 0);
+}
+
+int solattn_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
+                    int64_t N, int64_t d, int64_t prefix_len, float tau, int mode, int dtype,
+                    void* stream) {
+    int rc = validate(q, k, v, out, true, B, H, N, d, prefix_len, tau, mode, dtype);
+    if (rc) return rc;
+    void* ws = nullptr;
+    const size_t need = ws_layout(B, H, N, d, dtype).total;
+    if ((rc = internal_ws(need, &ws))) return rc;
+    return solattn_forward_ws(q, k, v, out, B, H, N, d, prefix_len, tau, mode, dtype, ws, need,
+                              stream);
+}
+
+int solattn_prepare_ws(const void* q, const void* k, const void* v, int64_t B, int64_t H,
+                       int64_t N, int64_t d, int mode, int dtype, void* ws, size_t ws_bytes,
+                       void* stream) {
+    int rc = validate(q, k, v, nullptr, false, B, H, N, d, 0, 0.f, mode, dtype);
+    if (rc) return rc;
+    if ((rc = check_ws(ws, ws_bytes, B, H, N, d, dtype))) return rc;
+    return run_prepare(q, k, v, B, H, N, d, mode, dtype, ws, static_cast<hipStream_t>(stream), true);
+}
+
+int solattn_attend_ws(const void* q, const void* k, const void* v, void* out, int64_t B,
+                      int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau, int mode,
+                      int dtype, void* ws, size_t ws_bytes, void* stream) {
+    int rc = validate(q, k, v, out, true, B, H, N, d, prefix_len, tau, mode, dtype);
+    if (rc) return rc;
+    if ((rc = check_ws(ws, ws_bytes, B, H, N, d, dtype))) return rc;
+    return run_attend(q, k, v, out, B, H, N, d, prefix_len, tau, mode, dtype, ws,
+                      static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, 0);
+}
+
+int solattn_forward_debug(const void* q, const void* k, const void* v, void* out, int64_t B,
+                          int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau,
+                          int mode, int dtype, uint32_t* mask_out, float* score_out,
+                          float* thr_out, void* stream) {
+    int rc = validate(q, k, v, out, true, B, H, N, d, prefix_len, tau, mode, dtype);
+    if (rc) return rc;
+    void* ws = nullptr;
+    if ((rc = internal_ws(ws_layout(B, H, N, d, dtype).total, &ws))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = run_prepare(q, k, v, B, H, N, d, mode, dtype, ws, s, true))) return rc;
+    return run_attend(q, k, v, out, B, H, N, d, prefix_len, tau, mode, dtype, ws, s, mask_out,
+                      score_out, thr_out, 0);
+}
+
+int solattn_pool(const void* q, const void* k, const void* v, float* qbar, float* kbar,
+                 float* vbar, int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
+                 void* stream) {
+    int rc = validate(q, k, v, nullptr, false, B, H, N, d, 0, 0.f, SOLATTN_SPARSE, dtype);
+    if (rc) return rc;
+    void* ws = nullptr;
+    const WsLayout L = ws_layout(B, H, N, d, dtype);
+    if ((rc = internal_ws(L.total, &ws))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = run_prepare(q, k, v, B, H, N, d, SOLATTN_SPARSE, dtype, ws, s, false))) return rc;
+    const size_t bytes = sizeof(float) * B * H * ((N + 63) / 64) * d;
+    const struct { float* dst; size_t off; } outs[3] = {{qbar, L.qbar}, {kbar, L.kbar}, {vbar, L.vbar}};
+    for (const auto& o : outs) {
+        if (!o.dst) continue;
+        hipError_t e = hipMemcpyAsync(o.dst, at(ws, o.off), bytes, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    }
+    return SOLATTN_OK;
+}
+
+int solattn_route(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t N,
+                  int64_t d, int64_t prefix_len, float tau, int dtype, uint32_t* mask_out,
+                  float* score_out, float* thr_out, void* stream) {
+    int rc = validate(q, k, v, nullptr, false, B, H, N, d, prefix_len, tau, SOLATTN_SPARSE, dtype);
+    if (rc) return rc;
+    void* ws = nullptr;
+    if ((rc = internal_ws(ws_layout(B, H, N, d, dtype).total, &ws))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = run_prepare(q, k, v, B, H, N, d, SOLATTN_SPARSE, dtype, ws, s, false))) return rc;
+    return run_attend(q, k, v, nullptr, B, H, N, d, prefix_len, tau, SOLATTN_SPARSE, dtype, ws, s,
+                      mask_out, score_out, thr_out, 1);
+}
+
+const char* solattn_strerror(int code) {
+    switch (code) {
+        case SOLATTN_OK: return "ok";
+        case SOLATTN_EINVAL: return "invalid argument";
+        case SOLATTN_EUNSUPPORTED: return "unsupported configuration";
+        case SOLATTN_EHIP: return "HIP runtime error";
+        case SOLATTN_ENOMEM: return "out of device memory";
+        default: return "unknown error code";
+    }
+}
+
+const char* solattn_last_error(void) { return g_last_error.c_str(); }
+
+const char* solattn_version(void) { return "solattn-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -48,7 +48,7 @@ class Workload:
     prefix_len: int
     taus: tuple           # tau values the workload is run at
     grid: Optional[tuple]  # (T, Y, X) latent grid of the video tokens, None for iid
-    kind: str             # "iid_offset" or "field"
+    kind: str             # "iid_offset" (Q, K, V), "iid_qk_offset" (Q, K only) or "field"
 
     @property
     def nb(self) -> int:
@@ -96,13 +96,16 @@ def _rng(seed: int, b: int, h: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, b, h])))
 
 
-def _head_iid_offset(rng, N, D):
+def _head_iid_offset(rng, N, D, v_offset=True):
     out = []
     nb = (N + BLOCK - 1) // BLOCK
-    for _ in range(3):  # Q, K, V
+    for t in range(3):  # Q, K, V
         base = rng.standard_normal((N, D))
         offs = rng.standard_normal((nb, D)) * 1.5
-        out.append(base + np.repeat(offs, BLOCK, axis=0)[:N])
+        if t < 2 or v_offset:
+            out.append(base + np.repeat(offs, BLOCK, axis=0)[:N])
+        else:
+            out.append(base)
     return out
 
 
@@ -143,8 +146,8 @@ def make_inputs(w: Workload, seed: int, heads: Optional[Sequence[int]] = None,
     for b in range(w.B):
         for hi, h in enumerate(heads):
             rng = _rng(seed, b, h)
-            if w.kind == "iid_offset":
-                qq, kk, vv = _head_iid_offset(rng, w.N, w.D)
+            if w.kind in ("iid_offset", "iid_qk_offset"):
+                qq, kk, vv = _head_iid_offset(rng, w.N, w.D, v_offset=w.kind == "iid_offset")
             else:
                 qq, kk, vv = _head_field(rng, w.N, w.D, w.prefix_len, w.grid)
             q[b, hi], k[b, hi], v[b, hi] = qq, kk, vv
@@ -158,9 +161,11 @@ def make_inputs(w: Workload, seed: int, heads: Optional[Sequence[int]] = None,
     return q, k, v
 
 
-def custom(B, H, N, D, dtype="bf16", prefix_len=0, seed=0, kind="iid_offset",
+def custom(B, H, N, D, dtype="bf16", prefix_len=0, seed=0, kind="iid_qk_offset",
            grid=None) -> tuple:
-    """Inputs for an arbitrary shape (edge-case tests)."""
+    """Inputs for an arbitrary shape (edge-case tests).  Default kind: Q and K
+    i.i.d. N(0,1) plus a per-block N(0, 1.5^2) offset, V i.i.d. N(0,1) (unit
+    variance, the regime the bf16 tolerance is stated for)."""
     if kind == "field" and grid is None:
         n_video = N - prefix_len
         grid = (1, 1, max(1, n_video))

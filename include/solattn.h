@@ -1,0 +1,151 @@
+/*
+ * solattn.h -- C interface of the Sol-Attn block-sparse attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (forward only, non-causal, one scale 1/sqrt(d)):
+ *
+ *   Tokens of every (batch, head) slice are cut into 64-token blocks on the
+ *   query and on the key side (page "英伟达开源 Sol-H3，给 MiniMax-H3 加速，
+ *   5 秒视频 1.4 秒出", section 2.2; page "MiniMax 官宣 NVIDIA Sol 团队 H3
+ *   加速:5 秒视频 1.653 秒生成并开源", section "提速来自流水线每一段的叠加").
+ *   Nb = ceil(N/64); block j has n_j = min(64, N - 64j) tokens.
+ *
+ *   1. Pooling: qbar_j, kbar_j, vbar_j are the means of each block's rows
+ *      (page "NVIDIA 团队开源 Sol-H3 的 DGX Spark 版本", section "119.68 GiB
+ *      的内存池", Sol-Attn item: pooled K/V summaries).
+ *   2. Routing: s_ij = qbar_i . kbar_j / sqrt(d).  Query block i keeps key
+ *      block j when j < ceil(prefix_len/64) (the always-exact prefix of the
+ *      packed sequence) or s_ij >= mu_i + tau*sigma_i, where mu_i and sigma_i
+ *      are the mean and population standard deviation of row i over all Nb
+ *      key blocks.  tau = -inf keeps everything, tau = +inf only the prefix,
+ *      and sigma_i = 0 uses the threshold mu_i.
+ *   3. Kept blocks contribute exact softmax terms exp(q_r.k_t/sqrt(d)) v_t.
+ *   4. Each skipped block contributes one pooled term
+ *      n_j exp(q_r.kbar_j/sqrt(d)) vbar_j to the numerator and
+ *      n_j exp(q_r.kbar_j/sqrt(d)) to the denominator (the pages' pooled
+ *      correction, taken at zeroth order).
+ *   5. Routing, exact terms and pooled terms share one online softmax per
+ *      query row; no score map and no routing index is written to device
+ *      memory (only the debug entry point exports them).
+ *
+ * Conventions shared by every entry point:
+ *   - q, k, v, out: caller-owned device pointers to contiguous row-major
+ *     [B][H][N][d] tensors, all of element type `dtype`, 16-byte aligned.
+ *     Inputs are read only; `out` must not overlap any input.
+ *   - B, H, N >= 1; d is 64 or 128; 0 <= prefix_len <= N; N <= 262144.
+ *   - tau may be +-infinity; NaN is rejected.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *     work on it and return without synchronising; completion is observed
+ *     through the stream.
+ *   - Every argument is checked on the host before any device call; a
+ *     rejected call enqueues nothing and returns a nonzero code whose text
+ *     solattn_last_error() gives.
+ *   - Calls on different streams may run concurrently, except that the
+ *     entry points without a `ws` argument share one internal workspace per
+ *     device: concurrent calls of those on different streams race.
+ */
+#ifndef SOLATTN_H
+#define SOLATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define SOLATTN_OK 0
+#define SOLATTN_EINVAL 1       /* argument outside the documented domain */
+#define SOLATTN_EUNSUPPORTED 2 /* valid but not built (e.g. N > 262144) */
+#define SOLATTN_EHIP 3         /* HIP runtime or launch error */
+#define SOLATTN_ENOMEM 4       /* workspace allocation failed */
+
+/* mode */
+#define SOLATTN_DENSE 0  /* every key block exact (plain softmax attention) */
+#define SOLATTN_SPARSE 1 /* Sol-Attn routing */
+
+/* dtype */
+#define SOLATTN_F32 0
+#define SOLATTN_BF16 1
+
+/*
+ * Full forward pass: pooling (step 1) then the fused routing + attention
+ * kernel (steps 2-5).  In DENSE mode tau and prefix_len are ignored and no
+ * pooling is done.  Uses an internal per-device workspace that grows on
+ * demand (the growth synchronises the device once).
+ */
+int solattn_forward(const void* q, const void* k, const void* v, void* out, int64_t B,
+                    int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau, int mode,
+                    int dtype, void* stream);
+
+/* Bytes of workspace solattn_forward_ws needs for this shape and dtype. */
+size_t solattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
+
+/*
+ * solattn_forward with a caller-owned device workspace `ws` of `ws_bytes`
+ * bytes (at least solattn_workspace_bytes(), 256-byte aligned).  Allocates
+ * nothing.  `ws` must not be used by another call until this one completes
+ * on `stream`.
+ */
+int solattn_forward_ws(const void* q, const void* k, const void* v, void* out, int64_t B,
+                       int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau, int mode,
+                       int dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The two stages of solattn_forward_ws as separate launches, so that each
+ * can be timed on its own.  solattn_prepare_ws runs step 1 (pooling into the
+ * workspace; in DENSE mode only the value-tile relayout the attention kernel
+ * reads).  solattn_attend_ws runs steps 2-5 and reads what prepare left in
+ * the same workspace for the same q, k, v, shape, dtype and mode.
+ */
+int solattn_prepare_ws(const void* q, const void* k, const void* v, int64_t B, int64_t H,
+                       int64_t N, int64_t d, int mode, int dtype, void* ws, size_t ws_bytes,
+                       void* stream);
+int solattn_attend_ws(const void* q, const void* k, const void* v, void* out, int64_t B,
+                      int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau, int mode,
+                      int dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * solattn_forward plus an export of the routing each query block used, from
+ * the same device code: mask_out [B][H][Nb][ceil(Nb/32)] uint32 words (bit
+ * j%32 of word j/32 in row i is keep_ij), score_out [B][H][Nb][Nb] fp32
+ * scores s_ij, thr_out [B][H][Nb] fp32 thresholds (-inf / +inf for tau =
+ * -inf / +inf; -inf in DENSE mode, where the mask is all ones).  Any export
+ * pointer may be NULL.  For tests and measurement only.
+ */
+int solattn_forward_debug(const void* q, const void* k, const void* v, void* out, int64_t B,
+                          int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau,
+                          int mode, int dtype, uint32_t* mask_out, float* score_out,
+                          float* thr_out, void* stream);
+
+/*
+ * Step 1 alone: block means as fp32 [B][H][Nb][d] into caller buffers
+ * (any may be NULL).
+ */
+int solattn_pool(const void* q, const void* k, const void* v, float* qbar, float* kbar,
+                 float* vbar, int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
+                 void* stream);
+
+/*
+ * Steps 1-2 alone (the routing "setup": pooling and scoring, no attention),
+ * with the exports of solattn_forward_debug.  Uses the internal workspace.
+ */
+int solattn_route(const void* q, const void* k, const void* v, int64_t B, int64_t H,
+                  int64_t N, int64_t d, int64_t prefix_len, float tau, int dtype,
+                  uint32_t* mask_out, float* score_out, float* thr_out, void* stream);
+
+/* Static text of a return code. */
+const char* solattn_strerror(int code);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* solattn_last_error(void);
+
+/* Library version string. */
+const char* solattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOLATTN_H */

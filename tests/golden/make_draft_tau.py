@@ -1,0 +1,64 @@
+"""Calibrate tau for the draft-stage workload (672x384 latent geometry,
+32 heads x 32768 tokens, prefix 512) so that ~90 % of the (query block,
+video key block) pairs are skipped: the draft stage runs its sparse
+attention at 90 % video sparsity with 64-token blocks (page "NVIDIA 团队开源
+Sol-H3 的 DGX Spark 版本", section "潜空间直传").
+
+Uses only the oracle's routing (scores and masks in fp64) on the seeded
+inputs; writes draft_tau.json next to this script.
+Usage: python tests/golden/make_draft_tau.py
+"""
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import oracle  # noqa: E402
+from block_sparse_video_solattn_amd import inputs  # noqa: E402
+
+SEED = 4000
+TARGET = (0.895, 0.905)
+
+
+def video_skip_fraction(q, k, v, w, tau):
+    pb = (w.prefix_len + 63) // 64
+    skipped = total = 0
+    for h in range(q.shape[1]):
+        m = oracle.head(q[0, h], k[0, h], v[0, h], w.prefix_len, tau, want_out=False)["mask"]
+        skipped += int((m[:, pb:] == 0).sum())
+        total += m[:, pb:].size
+    return skipped / total
+
+
+def main():
+    w = inputs.WORKLOADS["draft"]
+    q, k, v = inputs.make_inputs(w, SEED)
+    lo, hi = 0.0, 4.0
+    tau = 2.0
+    for it in range(30):
+        tau = 0.5 * (lo + hi)
+        f = video_skip_fraction(q, k, v, w, tau)
+        print("tau %.6f  video skip %.4f" % (tau, f), flush=True)
+        if TARGET[0] <= f <= TARGET[1]:
+            break
+        if f < TARGET[0]:
+            lo = tau
+        else:
+            hi = tau
+    out = {"workload": "draft", "seed": SEED, "tau": round(tau, 6), "video_skip_fraction": f,
+           "target": list(TARGET),
+           "note": "tau chosen by bisection on [0, 4] with the oracle's routing; the draft "
+                   "stage's 90% video sparsity is from page 'NVIDIA 团队开源 Sol-H3 的 DGX Spark "
+                   "版本', section '潜空间直传'"}
+    with open(os.path.join(HERE, "draft_tau.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(out)
+
+
+if __name__ == "__main__":
+    main()

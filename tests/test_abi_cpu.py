@@ -1,0 +1,103 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/solattn.h declares, and rejects bad arguments on the host before any
+device call."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from conftest import ROOT, ensure_library
+
+HEADER = os.path.join(ROOT, "include", "solattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(solattn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    ensure_library()
+    from block_sparse_video_solattn_amd import _binding
+    return _binding
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(lib.EXPORTS)
+
+
+def test_version_and_strerror(lib):
+    assert "gfx950" in lib.solattn_version()
+    assert lib.solattn_strerror(0) == "ok"
+    assert lib.solattn_strerror(1) == "invalid argument"
+    assert lib.solattn_strerror(99) == "unknown error code"
+
+
+def test_workspace_bytes(lib):
+    ws = lib.solattn_workspace_bytes(1, 32, 16384, 128, 1)
+    # pooled fp32 (3 + transposed) + bf16 pooled operands + value tiles
+    assert ws >= 32 * 16384 * 128 * 2
+    assert lib.solattn_workspace_bytes(1, 1, 1024, 64, 0) > 0
+    assert lib.solattn_workspace_bytes(1, 1, 1024, 96, 1) == 0
+
+
+A = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced
+
+
+def fwd(lib, q=A, k=A + 0x100000, v=A + 0x200000, out=A + 0x300000, B=1, H=1, N=1024, d=64,
+        prefix=0, tau=1.0, mode=1, dtype=1):
+    return lib.raw_call("solattn_forward", q, k, v, out, B, H, N, d, prefix, ctypes.c_float(tau),
+                        mode, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(out=0), 1), (dict(B=0), 1), (dict(H=-1), 1), (dict(N=0), 1),
+    (dict(d=96), 1), (dict(prefix=-1), 1), (dict(prefix=1025), 1), (dict(tau=float("nan")), 1),
+    (dict(mode=2), 1), (dict(dtype=3), 1), (dict(q=A + 8), 1), (dict(out=A + 0x100), 1),
+    (dict(N=64 * 4096 + 1), 2),
+])
+def test_forward_rejects_before_device(lib, kw, code):
+    assert fwd(lib, **kw) == code
+    assert lib.solattn_last_error() != ""
+
+
+def test_other_entry_points_validate(lib):
+    f = ctypes.c_float
+    assert lib.raw_call("solattn_forward_ws", A, A + 0x100000, A + 0x200000, A + 0x300000,
+                        1, 1, 1024, 64, 0, f(1.0), 1, 1, None, 0, None) == 1  # NULL ws
+    assert lib.raw_call("solattn_forward_ws", A, A + 0x100000, A + 0x200000, A + 0x300000,
+                        1, 1, 1024, 64, 0, f(1.0), 1, 1, A + 0x400000, 16, None) == 1  # too small
+    assert lib.raw_call("solattn_prepare_ws", None, A, A, 1, 1, 64, 64, 1, 1, A, 1 << 30, None) == 1
+    assert lib.raw_call("solattn_attend_ws", A, A, A, A + 0x1000000, 1, 1, 64, 128, 0, f(math.nan),
+                        1, 1, A, 1 << 30, None) == 1
+    assert lib.raw_call("solattn_forward_debug", A, A, A, None, 1, 1, 64, 64, 0, f(1.0), 1, 1,
+                        None, None, None, None) == 1
+    assert lib.raw_call("solattn_pool", A, A, A, None, None, None, 1, 1, 64, 32, 1, None) == 1
+    assert lib.raw_call("solattn_route", A, A, A, 1, 1, 64, 64, 65, f(1.0), 1, None, None, None,
+                        None) == 1
+
+
+def test_import_without_library_fails_loudly(tmp_path):
+    # a copy of the Python package without the shared library refuses to import
+    import shutil
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "block_sparse_video_solattn_amd")
+    dst = tmp_path / "block_sparse_video_solattn_amd"
+    dst.mkdir()
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            shutil.copy(os.path.join(pkg, f), dst / f)
+    code = "import block_sparse_video_solattn_amd as m; m.solattn_forward"
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=str(tmp_path))
+    assert r.returncode != 0 and "not built" in r.stderr
