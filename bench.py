@@ -80,6 +80,8 @@ def main():
     ap.add_argument("--tau", type=float, default=1.25)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip dense / tau sweep / setup timing")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run one plain 256 MiB device copy first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this operator is measured at one GPU's share; "
@@ -103,6 +105,14 @@ def main():
     ws = torch.empty(sa.solattn_workspace_bytes(B, H, N, d, sa.BF16), dtype=torch.uint8,
                      device="cuda")
     stream = torch.cuda.current_stream()
+    if args.copy_calib:
+        # a plain copy of known size (256 MiB read + 256 MiB written): the
+        # FETCH_SIZE / WRITE_SIZE it reports give the counters' scale
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # routing of this call (outside the timed region) for the FLOP accounting
     words, _, _ = sa.solattn_route(qd, kd, vd, w.prefix_len, tau, want_scores=False)

@@ -24,6 +24,14 @@ if not os.path.exists(LIB_PATH):
         "libsolattn.so is not built (expected at %s); run "
         "`python -m block_sparse_video_solattn_amd.build`" % LIB_PATH)
 
+# Load torch first when it is present: the library then binds to the HIP
+# runtime torch already mapped instead of pulling in a second copy, which
+# could not share device state with torch's allocations and streams.
+try:
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover - torch is the expected host
+    torch = None
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p

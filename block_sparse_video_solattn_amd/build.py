@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsolattn.so")
-SOURCES = ["solattn_api.cpp", "pool.hip", "attn_bf16.hip", "attn_f32.hip"]
+SOURCES = ["solattn_api.cpp", "pool.hip", "route.hip", "attn_bf16.hip", "attn_f32.hip"]
 ARCH = "gfx950"
 
 
@@ -27,6 +27,10 @@ def flags():
         "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 instructions stay off (plain fp32 VALU only)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in arch VGPRs: the online-softmax rescale touches
+        # the output accumulator with VALU ops, and AGPR-resident accumulators
+        # made the compiler copy all of them to VGPRs on every loop iteration
+        "-mllvm", "-amdgpu-mfma-vgpr-form=true",
         "-Wall", "-Wno-unused-result",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     ]

@@ -10,13 +10,14 @@
 //     all 64 rows in one wave gives every K/V element loaded into registers
 //     64 rows of reuse;
 //   * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 with
-//     fp32 accumulation.  Q^T is parked in LDS in operand order; K rows are
-//     loaded straight into A-operand registers; V tiles come pre-arranged in
-//     A-operand order from the pooling pass, so P^T is the S^T accumulator
-//     converted to bf16 with no lane shuffles;
-//   * each 64-key tile is consumed as two 32-key halves, so the operands of
-//     one half plus the prefetch of the next fit the register file next to
-//     the 64 x d fp32 output accumulator;
+//     fp32 accumulation.  Q^T is parked in LDS in operand order.  Key and
+//     value tiles come pre-arranged in A-operand order from the pooling pass,
+//     so every operand load reads a contiguous 1 KiB run, and P^T is the S^T
+//     accumulator converted to bf16 with no lane shuffles;
+//   * each 64-key tile is consumed as two 32-key halves; a half's values are
+//     fetched behind its S^T products and the next half's keys behind its
+//     softmax, so keys and values are never live at once next to the 64 x d
+//     fp32 output accumulator;
 //   * skipped blocks enter as "pooled tiles": 64 pooled keys kbar_j (bf16)
 //     with logit bias log2(n_j), or -inf where block j is kept or padding.
 //     The pooled term n_j exp(c q.kbar_j) vbar_j is exactly a softmax column
@@ -25,9 +26,10 @@
 //   * the online softmax runs in log2 units (exp2) with a lazy rescale: the
 //     reference maximum moves only when the row maximum grows by more than
 //     2^8, which keeps P <= 256 in bf16 and skips most rescales of the
-//     accumulators;
+//     accumulators.  The denominator adds the bf16-rounded weights the MFMA
+//     consumes (v_dot2 against (1, 1)), so numerator and denominator agree;
 //   * workgroups are remapped so that the query blocks of one head run on
-//     one XCD and share its L2 for the kept K/V tiles.
+//     one XCD and share its L2 for the K/V tiles they keep.
 #include "common.h"
 #include "launch.h"
 #include "route.h"
@@ -39,10 +41,10 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;
 
-// One 32-key half of a 64-key tile.
+// One 32-key half of a 64-key tile (exact block or pooled tile).
 struct Half {
-    const bf16* krows;  // key row 0 of this half (exact) / pooled key 0 of this half
-    const bf16* vtile;  // operand-ordered value tile of the whole 64-key tile
+    const bf16* ktile;  // operand-ordered key tile
+    const bf16* vtile;  // operand-ordered value tile
     int u;              // which half (0, 1)
     int kind;           // 0 exact, 1 exact with masked keys, 2 pooled
     int nvalid;         // kind 1: valid keys in this half (1..31)
@@ -50,12 +52,11 @@ struct Half {
 };
 
 template <int D>
-__device__ inline void load_k(const Half& h, int l32, int half, bf16x8 (&kA)[D / 16]) {
-    int r = l32;
-    if (h.kind == 1 && r >= h.nvalid) r = h.nvalid - 1;  // stay inside the tensor
-    const bf16* row = h.krows + (int64_t)r * D + 8 * half;
+__device__ inline void load_k(const Half& h, int lane, bf16x8 (&kA)[D / 16]) {
+    constexpr int KS = D / 16;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) kA[s] = *reinterpret_cast<const bf16x8*>(row + 16 * s);
+    for (int s = 0; s < KS; ++s)
+        kA[s] = *reinterpret_cast<const bf16x8*>(h.ktile + ktile_offset(KS, h.u, s, lane, 0));
 }
 
 template <int D>
@@ -95,12 +96,11 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
         n_kept = (int)Nb;
         tile_mask = 0;
     }
-    if (a.route_only) return;
 
     const bf16* qp = reinterpret_cast<const bf16*>(a.q) + bh * N * D;
-    const bf16* kp = reinterpret_cast<const bf16*>(a.k) + bh * N * D;
+    const bf16* kp = reinterpret_cast<const bf16*>(a.kP) + bh * Nb * D * 64;
     const bf16* vp = reinterpret_cast<const bf16*>(a.vP) + bh * Nb * D * 64;
-    const bf16* kbp = reinterpret_cast<const bf16*>(a.kbar16) + bh * Nbp * D;
+    const bf16* kbp = reinterpret_cast<const bf16*>(a.kbarP) + bh * Nbp * D;
     const bf16* vbp = reinterpret_cast<const bf16*>(a.vbarP) + bh * Nbp * D;
     const int tail = (int)(N - (Nb - 1) * 64);  // keys in the last block (1..64)
 
@@ -128,13 +128,17 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     float mref[2] = {-__builtin_inff(), -__builtin_inff()};
     float lsum[2] = {0.f, 0.f};
     const float scale2 = kLog2e / sqrtf((float)D);
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
     // Sequence of halves: exact tiles in kept-list order, then the pooled
     // tiles holding a skipped block in ascending order.  An exact tail tile of
     // <= 32 keys has only its first half.
     const int n_tiles = n_kept + __popcll(tile_mask);
+    // (the kept-list entry is wave-uniform: readfirstlane keeps the tile
+    // pointers in scalar registers)
     auto exact_block = [&](int t) -> int64_t {
-        return (a.mode == kSparse) ? (int64_t)klist[t] : (int64_t)t;
+        return (a.mode == kSparse) ? (int64_t)__builtin_amdgcn_readfirstlane((int)klist[t])
+                                   : (int64_t)t;
     };
     auto half_at = [&](int t, int u, int T) -> Half {
         Half h;
@@ -142,13 +146,13 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
         if (t < n_kept) {
             const int64_t j = exact_block(t);
             const int nv = ((j == Nb - 1) ? tail : 64) - 32 * u;
-            h.krows = kp + (j * 64 + 32 * u) * D;
+            h.ktile = kp + j * (int64_t)D * 64;
             h.vtile = vp + j * (int64_t)D * 64;
             h.kind = nv < 32 ? 1 : 0;
             h.nvalid = nv;
             h.bias_off = 0;
         } else {
-            h.krows = kbp + ((int64_t)T * 64 + 32 * u) * D;
+            h.ktile = kbp + (int64_t)T * D * 64;
             h.vtile = vbp + (int64_t)T * D * 64;
             h.kind = 2;
             h.nvalid = 32;
@@ -165,10 +169,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     bf16x8 kA[KS];
     bf16x8 vA[MT][2];
     Half h = half_at(0, 0, pT);
-    if (n_tiles > 0) {
-        load_k<D>(h, l32, half, kA);
-        load_v<D>(h, lane, vA);
-    }
+    load_k<D>(h, lane, kA);
 
     while (t < n_tiles) {
         // which half comes next
@@ -178,8 +179,6 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
             un = 0;
             if (t >= n_kept) {  // leaving pooled tile pT
                 ptm &= ptm - 1;
-                pTn = ptm ? __builtin_ctzll(ptm) : 0;
-            } else if (tn == n_kept) {
                 pTn = ptm ? __builtin_ctzll(ptm) : 0;
             }
         }
@@ -201,10 +200,12 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
             st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[s], q0, st[0], 0, 0, 0);
             st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[s], q1, st[1], 0, 0, 0);
         }
-        // K registers are free again: fetch the next half's keys
-        if (more) load_k<D>(hn, l32, half, kA);
+        // this half's values, needed after the softmax (the scheduling barrier
+        // keeps the loads behind the S^T products)
+        __builtin_amdgcn_sched_barrier(0);
+        load_v<D>(h, lane, vA);
 
-        // Logits in log2 units are fma(st, sc, bias).  Pooled halves add the
+        // Logits in log2 units are st * sc (+ bias).  Pooled halves add the
         // per-key bias log2(n_j) / -inf here (sc becomes 1); the exact tail
         // masks keys past the block; exact halves keep the raw scores and
         // fold the scale into the exp2 argument.  Register v holds key
@@ -232,11 +233,15 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
             }
         }
 
+        // online softmax of both query halves -> P^T (bf16), the B operand of
+        // the PV product: k-step s holds keys 16*s + 4*half + {0..3, 8..11} of
+        // this half = accumulator registers 8*s .. 8*s+7
+        bf16x8 pB[2][2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            float mx = -__builtin_inff();
+            float mx = fmaxf(st[nt][0], st[nt][1]);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[nt][v]);
+            for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(st[nt][v], st[nt][v + 1]));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc;
             const float mcand = fmaxf(mref[nt], mx);
             const bool grow = mcand > mref[nt] + kRescaleSlack;
@@ -250,37 +255,38 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
                     for (int v = 0; v < 16; ++v) oacc[mt][nt][v] *= alpha;
                 mref[nt] = mnew;
             }
-            // P^T, B operand of the PV product: k-step s holds keys
-            // 16*s + 4*half + {0..3, 8..11} of this half = registers 8*s .. 8*s+7.
-            // The denominator sums the bf16-rounded weights the MFMA uses, so
-            // numerator and denominator see identical weights.
             // (A pooled half whose keys are all kept blocks has only -inf
             // logits; while no finite logit has been seen, subtract 0 so that
             // such a half yields p = 0 rather than exp2(-inf + inf).)
             const float msub = mref[nt] == -__builtin_inff() ? 0.f : mref[nt];
-            float ps = 0.f;
-            bf16x8 pB[2];
+            float ps = lsum[nt];
 #pragma unroll
             for (int v = 0; v < 16; v += 2) {
                 f32x2 pp;
                 pp[0] = __builtin_amdgcn_exp2f(st[nt][v] * sc - msub);
                 pp[1] = __builtin_amdgcn_exp2f(st[nt][v + 1] * sc - msub);
                 const bf16x2 pr = __builtin_convertvector(pp, bf16x2);
-                const uint32_t bits = __builtin_bit_cast(uint32_t, pr);
-                ps += __uint_as_float(bits << 16) + __uint_as_float(bits & 0xffff0000u);
-                pB[v >> 3][v & 7] = pr[0];
-                pB[v >> 3][(v & 7) + 1] = pr[1];
+                ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
+                pB[nt][v >> 3][v & 7] = pr[0];
+                pB[nt][v >> 3][(v & 7) + 1] = pr[1];
             }
-            lsum[nt] += ps;
-            // O^T += V^T P^T for this query half
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    oacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vA[mt][s], pB[s],
-                                                                           oacc[mt][nt], 0, 0, 0);
+            lsum[nt] = ps;
         }
-        if (more) load_v<D>(hn, lane, vA);
+
+        // the K registers are free: fetch the next half's keys while the PV
+        // products run
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) load_k<D>(hn, lane, kA);
+
+        // O^T += V^T P^T
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    oacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vA[mt][s], pB[nt][s],
+                                                                           oacc[mt][nt], 0, 0, 0);
         h = hn;
         t = tn;
         u = un;

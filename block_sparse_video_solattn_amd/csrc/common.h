@@ -43,6 +43,15 @@ __host__ __device__ inline void vtile_slot(int kk, int* s, int* half, int* e) {
     *e = (r & 3) + 4 * (r >> 3);
 }
 
+// Element offset of (u, s, lane, e) inside one 64-key key tile laid out in the
+// A-operand order of v_mfma_f32_32x32x16_bf16 for S^T = K Q^T, consumed in
+// 32-key halves u: 16-byte group (u*KS + s)*64 + lane (KS = d/16) holds
+// K[32*u + lane%32][16*s + 8*(lane/32) + e], e = 0..7 -- a whole 16-byte chunk
+// of one key row, so the relayout only permutes chunks.
+__host__ __device__ inline int ktile_offset(int KS, int u, int s, int lane, int e) {
+    return ((u * KS + s) * 64 + lane) * 8 + e;
+}
+
 // Round-to-nearest-even fp32 -> bf16 (finite inputs).
 __device__ inline bf16 to_bf16(float x) { return (bf16)x; }
 

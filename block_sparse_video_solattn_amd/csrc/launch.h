@@ -16,11 +16,12 @@ enum Mode { kDense = 0, kSparse = 1 };
 //   qbar, kbar, vbar  fp32 [BH][Nb][d]     block means
 //   kbarT             fp32 [BH][d][Nbp]    block means of K, transposed for the
 //                                          coalesced score pass; zero padded
-//   kbar16            bf16 [BH][Nbp][d]    pooled keys, MFMA operand (bf16 only)
+//   kbarP             bf16 [BH][Nbp/64][64*d] pooled keys, MFMA operand order (bf16 only)
 //   vbarP             bf16 [BH][Nbp/64][d*64] pooled values, MFMA operand order
+//   kP                bf16 [BH][Nb][64*d]  key tiles, MFMA operand order
 //   vP                bf16 [BH][Nb][d*64]  value tiles, MFMA operand order
 struct WsLayout {
-    size_t qbar, kbar, vbar, kbarT, kbar16, vbarP, vP, total;
+    size_t qbar, kbar, vbar, kbarT, kbarP, vbarP, kP, vP, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -35,11 +36,12 @@ inline WsLayout ws_layout(int64_t B, int64_t H, int64_t N, int64_t d, int dtype)
     w.vbar = take(sizeof(float) * BH * Nb * d);
     w.kbarT = take(sizeof(float) * BH * d * Nbp);
     if (dtype == kBF16) {
-        w.kbar16 = take(2 * BH * Nbp * d);
+        w.kbarP = take(2 * BH * Nbp * d);
         w.vbarP = take(2 * BH * Nbp * d);
+        w.kP = take(2 * BH * Nb * 64 * d);
         w.vP = take(2 * BH * Nb * 64 * d);
     } else {
-        w.kbar16 = w.vbarP = w.vP = 0;
+        w.kbarP = w.vbarP = w.kP = w.vP = 0;
     }
     w.total = off;
     return w;
@@ -53,21 +55,23 @@ struct PoolArgs {
     float* kbar;
     float* vbar;
     float* kbarT;
-    void* kbar16;
+    void* kbarP;
     void* vbarP;
+    void* kP;
     void* vP;
     int64_t N, Nb, Nbp;
     int d, dtype;
     int pooled;   // compute block means (sparse mode)
-    int pack_v;   // write the operand-ordered value tiles (bf16)
+    int pack;     // write the operand-ordered key and value tiles (bf16)
 };
 
 struct AttnArgs {
     const void* q;
     const void* k;
-    const void* vP;       // bf16: value tiles; f32: unused
+    const void* kP;       // bf16: key tiles in operand order; f32: unused
+    const void* vP;       // bf16: value tiles in operand order; f32: unused
     const void* v;        // f32 path reads V directly
-    const void* kbar16;
+    const void* kbarP;
     const void* vbarP;
     const float* kbar;    // f32 path pooled operands
     const float* vbar;
@@ -81,10 +85,10 @@ struct AttnArgs {
     int64_t Pb;
     float tau;
     int d, dtype, mode;
-    int route_only;       // stop after routing (setup timing / export)
 };
 
 hipError_t launch_pool(const PoolArgs& a, int64_t BH, hipStream_t s);
+hipError_t launch_route(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 

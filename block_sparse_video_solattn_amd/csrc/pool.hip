@@ -75,102 +75,129 @@ __device__ inline void reduce_mean(const float (&acc)[Vec16<T>::n], int n, int t
     __syncthreads();
 }
 
+// Relayout of one staged 64-row tile (LDS, row-major, zero rows past the
+// block) into MFMA operand order; consecutive threads write consecutive
+// 16-byte groups.
+template <int D>
+__device__ inline void write_key_tile(const bf16 (*tile)[D + 8], bf16* dst, int tid) {
+    constexpr int KS = D / 16;
+    for (int g = tid; g < D * 8; g += 256) {
+        const int lane = g & 63, us = g >> 6;
+        const int u = us / KS, s = us % KS;
+        const int row = 32 * u + (lane & 31), col = 16 * s + 8 * (lane >> 5);
+        *reinterpret_cast<bf16x8*>(dst + g * 8) = *reinterpret_cast<const bf16x8*>(&tile[row][col]);
+    }
+}
+
+template <int D>
+__device__ inline void write_value_tile(const bf16 (*tile)[D + 8], bf16* dst, int tid) {
+    for (int g = tid; g < D * 8; g += 256) {
+        const int lane = g & 63, ms = g >> 6;
+        const int mt = ms >> 2, s = ms & 3;
+        const int dcol = 32 * mt + (lane & 31), half = lane >> 5;
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = tile[vtile_key(s, half, e)][dcol];
+        *reinterpret_cast<bf16x8*>(dst + g * 8) = o;
+    }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     constexpr int VEC = Vec16<T>::n;
     constexpr int CPR = D / VEC;
     constexpr int RPP = 256 / CPR;
     constexpr int PASSES = 64 / RPP;
+    constexpr int KS = D / 16;
     __shared__ float red[RPP * D];
     __shared__ float mean[D];
-    __shared__ bf16 vt[64][D + 8];  // value tile staging for the relayout (bf16 only)
+    __shared__ bf16 tile[64][D + 8];  // staging for the operand relayout (bf16 only)
 
     const int tid = threadIdx.x;
     const int64_t j = blockIdx.x, bh = blockIdx.y;
     const int64_t Nb = a.Nb, Nbp = a.Nbp, N = a.N;
+    const bool bf = a.dtype == kBF16;
+
+    // pooled-operand slot of pooled key j (tile j/64, key j%64 of that tile)
+    const int kk = (int)(j & 63);
+    bf16* kbarP = bf ? reinterpret_cast<bf16*>(a.kbarP) + (bh * (Nbp / 64) + j / 64) * D * 64 : nullptr;
+    bf16* vbarP = bf ? reinterpret_cast<bf16*>(a.vbarP) + (bh * (Nbp / 64) + j / 64) * D * 64 : nullptr;
+    auto put_pooled = [&](int dcol, float km, float vm) {
+        // key: row kk of the tile, column dcol
+        const int s = dcol / 16, half = (dcol / 8) & 1, e = dcol & 7;
+        kbarP[ktile_offset(KS, kk / 32, s, 32 * half + (kk & 31), e)] = to_bf16(km);
+        int vs, vh, ve;
+        vtile_slot(kk, &vs, &vh, &ve);
+        vbarP[vtile_offset(dcol / 32, vs, 32 * vh + (dcol & 31), ve)] = to_bf16(vm);
+    };
 
     if (j >= Nb) {
-        // padding of the pooled-key tiles: zero keys and values (their logits
-        // are masked to -inf, zeros keep 0 * value finite)
+        // padding of the pooled tiles: zero keys and values (their logits are
+        // masked to -inf; zeros keep 0 * value finite)
         if (!a.pooled) return;
         if (tid < D) {
             a.kbarT[(bh * D + tid) * Nbp + j] = 0.f;
-            if (a.dtype == kBF16) {
-                reinterpret_cast<bf16*>(a.kbar16)[(bh * Nbp + j) * D + tid] = (bf16)0.f;
-                int s, half, e, kk = (int)(j & 63);
-                vtile_slot(kk, &s, &half, &e);
-                const int mt = tid / 32, lane = 32 * half + (tid & 31);
-                reinterpret_cast<bf16*>(a.vbarP)[(bh * (Nbp / 64) + j / 64) * D * 64 +
-                                                 vtile_offset(mt, s, lane, e)] = (bf16)0.f;
-            }
+            if (bf) put_pooled(tid, 0.f, 0.f);
         }
         return;
     }
 
     const int n = (int)((j + 1) * 64 <= N ? 64 : N - j * 64);
     const int64_t row0 = bh * N + j * 64;
+    const bool pack = bf && a.pack;
     float acc[VEC];
+    typename Vec16<T>::type keep[PASSES];
+    auto stage = [&]() {
+        const int c = tid % CPR, r0 = tid / CPR;
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) tile[r0 + p * RPP][c * VEC + e] = (bf16)keep[p][e];
+    };
 
     if (a.pooled) {
-        // Q
         load_rows<T, D>(reinterpret_cast<const T*>(a.q) + row0 * D, n, tid, acc, nullptr);
         reduce_mean<T, D>(acc, n, tid, red, mean);
         if (tid < D) a.qbar[(bh * Nb + j) * D + tid] = mean[tid];
-        // K
-        load_rows<T, D>(reinterpret_cast<const T*>(a.k) + row0 * D, n, tid, acc, nullptr);
-        reduce_mean<T, D>(acc, n, tid, red, mean);
-        if (tid < D) {
-            const float m = mean[tid];
-            a.kbar[(bh * Nb + j) * D + tid] = m;
-            a.kbarT[(bh * D + tid) * Nbp + j] = m;
-            if (a.dtype == kBF16) reinterpret_cast<bf16*>(a.kbar16)[(bh * Nbp + j) * D + tid] = to_bf16(m);
+    }
+    // K: means, and the operand-ordered key tile
+    if (a.pooled || pack) {
+        load_rows<T, D>(reinterpret_cast<const T*>(a.k) + row0 * D, n, tid, acc, keep);
+        if (a.pooled) {
+            reduce_mean<T, D>(acc, n, tid, red, mean);
+            if (tid < D) {
+                a.kbar[(bh * Nb + j) * D + tid] = mean[tid];
+                a.kbarT[(bh * D + tid) * Nbp + j] = mean[tid];
+            }
+        }
+        if (pack) {
+            stage();
+            __syncthreads();
+            write_key_tile<D>(tile, reinterpret_cast<bf16*>(a.kP) + (bh * Nb + j) * (int64_t)D * 64, tid);
+            __syncthreads();
         }
     }
-    // V (means and/or the operand-ordered tile)
-    typename Vec16<T>::type keep[PASSES];
+    // V: means, and the operand-ordered value tile
     load_rows<T, D>(reinterpret_cast<const T*>(a.v) + row0 * D, n, tid, acc, keep);
     if (a.pooled) {
+        const float km = tid < D ? mean[tid] : 0.f;  // K mean, still in LDS
+        __syncthreads();
         reduce_mean<T, D>(acc, n, tid, red, mean);
         if (tid < D) {
-            const float m = mean[tid];
-            a.vbar[(bh * Nb + j) * D + tid] = m;
-            if (a.dtype == kBF16) {
-                int s, half, e, kk = (int)(j & 63);
-                vtile_slot(kk, &s, &half, &e);
-                const int mt = tid / 32, lane = 32 * half + (tid & 31);
-                reinterpret_cast<bf16*>(a.vbarP)[(bh * (Nbp / 64) + j / 64) * D * 64 +
-                                                 vtile_offset(mt, s, lane, e)] = to_bf16(m);
-            }
+            a.vbar[(bh * Nb + j) * D + tid] = mean[tid];
+            if (bf) put_pooled(tid, km, mean[tid]);
         }
     }
-    if constexpr (sizeof(T) == 2) {
-        if (a.pack_v) {
-            const int c = tid % CPR, r0 = tid / CPR;
-#pragma unroll
-            for (int p = 0; p < PASSES; ++p) {
-                const int r = r0 + p * RPP;
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) vt[r][c * VEC + e] = keep[p][e];
-            }
-            __syncthreads();
-            // 16-byte output groups: D*64/8 of them, consecutive threads write
-            // consecutive groups
-            bf16* dst = reinterpret_cast<bf16*>(a.vP) + (bh * Nb + j) * (int64_t)D * 64;
-            for (int gidx = tid; gidx < D * 8; gidx += 256) {
-                const int lane = gidx & 63, ms = gidx >> 6;
-                const int mt = ms >> 2, s = ms & 3;
-                const int dcol = 32 * mt + (lane & 31), half = lane >> 5;
-                bf16x8 o;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] = vt[vtile_key(s, half, e)][dcol];
-                *reinterpret_cast<bf16x8*>(dst + gidx * 8) = o;
-            }
-        }
+    if (pack) {
+        stage();
+        __syncthreads();
+        write_value_tile<D>(tile, reinterpret_cast<bf16*>(a.vP) + (bh * Nb + j) * (int64_t)D * 64, tid);
     }
 }
 
 hipError_t launch_pool(const PoolArgs& a, int64_t BH, hipStream_t s) {
     const dim3 grid((unsigned)(a.pooled ? a.Nbp : a.Nb), (unsigned)BH);
+    if (a.dtype != kBF16 && !a.pooled) return hipSuccess;
     if (a.dtype == kBF16) {
         if (a.d == 128)
             hipLaunchKernelGGL((pool_kernel<bf16, 128>), grid, dim3(256), 0, s, a);

@@ -117,7 +117,7 @@ int internal_ws(size_t need, void** out) {
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 int run_prepare(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t N,
-                int64_t d, int mode, int dtype, void* ws, hipStream_t s, bool pack_v) {
+                int64_t d, int mode, int dtype, void* ws, hipStream_t s, bool pack) {
     const WsLayout L = ws_layout(B, H, N, d, dtype);
     PoolArgs p;
     p.q = q;
@@ -127,8 +127,9 @@ int run_prepare(const void* q, const void* k, const void* v, int64_t B, int64_t 
     p.kbar = reinterpret_cast<float*>(at(ws, L.kbar));
     p.vbar = reinterpret_cast<float*>(at(ws, L.vbar));
     p.kbarT = reinterpret_cast<float*>(at(ws, L.kbarT));
-    p.kbar16 = dtype == kBF16 ? at(ws, L.kbar16) : nullptr;
+    p.kbarP = dtype == kBF16 ? at(ws, L.kbarP) : nullptr;
     p.vbarP = dtype == kBF16 ? at(ws, L.vbarP) : nullptr;
+    p.kP = dtype == kBF16 ? at(ws, L.kP) : nullptr;
     p.vP = dtype == kBF16 ? at(ws, L.vP) : nullptr;
     p.N = N;
     p.Nb = (N + 63) / 64;
@@ -136,8 +137,8 @@ int run_prepare(const void* q, const void* k, const void* v, int64_t B, int64_t 
     p.d = (int)d;
     p.dtype = dtype;
     p.pooled = mode == SOLATTN_SPARSE;
-    p.pack_v = pack_v && dtype == kBF16;
-    if (!p.pooled && !p.pack_v) return SOLATTN_OK;  // fp32 dense: nothing to prepare
+    p.pack = pack && dtype == kBF16;
+    if (!p.pooled && !p.pack) return SOLATTN_OK;  // fp32 dense: nothing to prepare
     hipError_t e = launch_pool(p, B * H, s);
     if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
     return SOLATTN_OK;
@@ -152,8 +153,9 @@ int run_attend(const void* q, const void* k, const void* v, void* out, int64_t B
     a.q = q;
     a.k = k;
     a.v = v;
+    a.kP = dtype == kBF16 ? at(ws, L.kP) : nullptr;
     a.vP = dtype == kBF16 ? at(ws, L.vP) : nullptr;
-    a.kbar16 = dtype == kBF16 ? at(ws, L.kbar16) : nullptr;
+    a.kbarP = dtype == kBF16 ? at(ws, L.kbarP) : nullptr;
     a.vbarP = dtype == kBF16 ? at(ws, L.vbarP) : nullptr;
     a.kbar = reinterpret_cast<const float*>(at(ws, L.kbar));
     a.vbar = reinterpret_cast<const float*>(at(ws, L.vbar));
@@ -172,9 +174,9 @@ int run_attend(const void* q, const void* k, const void* v, void* out, int64_t B
     a.d = (int)d;
     a.dtype = dtype;
     a.mode = mode;
-    a.route_only = route_only;
-    hipError_t e = dtype == kBF16 ? launch_attn_bf16(a, s) : launch_attn_f32(a, s);
-    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    hipError_t e = route_only ? launch_route(a, s)
+                              : dtype == kBF16 ? launch_attn_bf16(a, s) : launch_attn_f32(a, s);
+    if (e != hipSuccess) return hip_fail(e, route_only ? "route kernel launch" : "attention kernel launch");
     return SOLATTN_OK;
 }
 
