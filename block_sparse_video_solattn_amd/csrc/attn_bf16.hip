@@ -41,32 +41,151 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;
 
-// One 32-key half of a 64-key tile (exact block or pooled tile).
-struct Half {
+// One 64-key tile of the sequence: an exact key block or a pooled tile.
+struct TileRef {
     const bf16* ktile;  // operand-ordered key tile
     const bf16* vtile;  // operand-ordered value tile
-    int u;              // which half (0, 1)
-    int kind;           // 0 exact, 1 exact with masked keys, 2 pooled
-    int nvalid;         // kind 1: valid keys in this half (1..31)
-    int bias_off;       // kind 2: srow index of key 0 of this half
+    int nvalid;         // keys in the block (64, or 1..63 for an exact tail block)
+    int bias_off;       // LDS index (bias array) of key 0 of the tile
 };
 
 template <int D>
-__device__ inline void load_k(const Half& h, int lane, bf16x8 (&kA)[D / 16]) {
+__device__ inline void load_k(const TileRef& t, int u, int lane, bf16x8 (&kA)[D / 16]) {
     constexpr int KS = D / 16;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-        kA[s] = *reinterpret_cast<const bf16x8*>(h.ktile + ktile_offset(KS, h.u, s, lane, 0));
+        kA[s] = *reinterpret_cast<const bf16x8*>(t.ktile + ktile_offset(KS, u, s, lane, 0));
 }
 
 template <int D>
-__device__ inline void load_v(const Half& h, int lane, bf16x8 (&vA)[D / 32][2]) {
+__device__ inline void load_v(const TileRef& t, int u, int lane, bf16x8 (&vA)[D / 32][2]) {
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-            vA[mt][s] = *reinterpret_cast<const bf16x8*>(h.vtile +
-                                                         vtile_offset(mt, 2 * h.u + s, lane, 0));
+            vA[mt][s] = *reinterpret_cast<const bf16x8*>(t.vtile + vtile_offset(mt, 2 * u + s, lane, 0));
+}
+
+// Shared state of one wave's 64 query rows.
+template <int D>
+struct RowState {
+    f32x16 oacc[D / 32][2];  // O^T accumulators: d = 32*mt + ..., queries 32*nt + l32
+    float mref[2];           // reference maximum (log2 units) per query half
+    float lsum[2];           // this lane's share of the denominator per query half
+};
+
+// One 32-key half u of tile `cur`: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// Right after the S^T products it issues the prefetches: the same half of the
+// next tile into kA, and the value operands the next half needs into vNext
+// (half 1 of this tile when u = 0, half 0 of the next tile when u = 1).
+template <int D>
+__device__ __forceinline__ void half_step(int u, const TileRef& cur, const TileRef& nxt, bool more,
+                                          const bf16x8* __restrict__ qs, const float* srow,
+                                          int lane, int half, float scale2,
+                                          bf16x8 (&kA)[D / 16], bf16x8 (&vUse)[D / 32][2],
+                                          bf16x8 (&vNext)[D / 32][2], RowState<D>& rs) {
+    constexpr int KS = D / 16;
+    constexpr int MT = D / 32;
+    // S^T: 32 keys x 64 queries, two 32x32 accumulators; Q^T from LDS
+    f32x16 st[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st[nt][v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const bf16x8 q0 = qs[s * 64 + lane];
+        const bf16x8 q1 = qs[(KS + s) * 64 + lane];
+        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[s], q0, st[0], 0, 0, 0);
+        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[s], q1, st[1], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) load_k<D>(nxt, u, lane, kA);
+    if (u == 0)
+        load_v<D>(cur, 1, lane, vNext);
+    else if (more)
+        load_v<D>(nxt, 0, lane, vNext);
+
+    // Logits in log2 units: st * scale2 + bias, with the per-key bias read
+    // from LDS for every tile: 0 for exact keys, -inf for the zero-padded
+    // keys past an exact tail block, log2(n_j) / -inf for pooled keys (kept
+    // blocks and padding masked).  Register v of an accumulator holds key
+    // 32*u + 8*(v/4) + 4*half + v%4 of the tile.
+    {
+        const float* b = srow + cur.bias_off + 32 * u + 4 * half;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 bb = *reinterpret_cast<const f32x4*>(b + 8 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    st[nt][4 * g + r] = st[nt][4 * g + r] * scale2 + bb[r];
+        }
+    }
+
+    // online softmax of both query halves -> P^T (bf16), the B operand of the
+    // PV product: k-step s holds keys 16*s + 4*half + {0..3, 8..11} of this
+    // half = accumulator registers 8*s .. 8*s+7.  The denominator adds the
+    // bf16-rounded weights the MFMA consumes (v_dot2 against (1, 1)).
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    bf16x8 pB[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        float mx = fmaxf(st[nt][0], st[nt][1]);
+#pragma unroll
+        for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(st[nt][v], st[nt][v + 1]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mcand = fmaxf(rs.mref[nt], mx);
+        const bool grow = mcand > rs.mref[nt] + kRescaleSlack;
+        if (__ballot(grow)) {
+            const float mnew = grow ? mcand : rs.mref[nt];
+            const float alpha = __builtin_amdgcn_exp2f(rs.mref[nt] - mnew);
+            rs.lsum[nt] *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) rs.oacc[mt][nt][v] *= alpha;
+            rs.mref[nt] = mnew;
+        }
+        // (while no finite logit has been seen -- a pooled or tail half whose
+        // keys are all masked -- subtract 0 so the half yields p = 0 rather
+        // than exp2(-inf + inf))
+        const float msub = rs.mref[nt] == -__builtin_inff() ? 0.f : rs.mref[nt];
+        float ps = rs.lsum[nt];
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+            f32x2 pp;
+            pp[0] = __builtin_amdgcn_exp2f(st[nt][v] - msub);
+            pp[1] = __builtin_amdgcn_exp2f(st[nt][v + 1] - msub);
+            const bf16x2 pr = __builtin_convertvector(pp, bf16x2);
+            ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
+            pB[nt][v >> 3][v & 7] = pr[0];
+            pB[nt][v >> 3][(v & 7) + 1] = pr[1];
+        }
+        rs.lsum[nt] = ps;
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                rs.oacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vUse[mt][s], pB[nt][s],
+                                                                          rs.oacc[mt][nt], 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void tile_step(const TileRef& cur, const TileRef& nxt, bool more,
+                                          const bf16x8* __restrict__ qs, const float* srow,
+                                          int lane, int half, float scale2,
+                                          bf16x8 (&kA0)[D / 16], bf16x8 (&kA1)[D / 16],
+                                          bf16x8 (&vA0)[D / 32][2], bf16x8 (&vA1)[D / 32][2],
+                                          RowState<D>& rs) {
+    half_step<D>(0, cur, nxt, more, qs, srow, lane, half, scale2, kA0, vA0, vA1, rs);
+    half_step<D>(1, cur, nxt, more, qs, srow, lane, half, scale2, kA1, vA1, vA0, rs);
 }
 
 }  // namespace
@@ -81,9 +200,13 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     const int64_t N = a.N, Nb = a.Nb, Nbp = a.Nbp;
     const int64_t w = xcd_remap(blockIdx.x, a.BH * Nb);
     const int64_t bh = w / Nb, i = w % Nb;
+    // LDS: srow[Nbp] routing scores, then pooled-key biases; two 64-entry
+    // bias rows for exact tiles (all zero; zero then -inf past the tail
+    // block's last key); the kept list; Q^T in operand order
     float* srow = smem;
-    uint16_t* klist = reinterpret_cast<uint16_t*>(smem + Nbp);
-    bf16x8* qs = reinterpret_cast<bf16x8*>(smem + Nbp + (Nb + 15) / 16 * 8);
+    const int zero_bias = (int)Nbp, tail_bias = (int)Nbp + 64;
+    uint16_t* klist = reinterpret_cast<uint16_t*>(smem + Nbp + 128);
+    bf16x8* qs = reinterpret_cast<bf16x8*>(smem + Nbp + 128 + (Nb + 15) / 16 * 8);
 
     int n_kept;
     uint64_t tile_mask;
@@ -103,6 +226,8 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     const bf16* kbp = reinterpret_cast<const bf16*>(a.kbarP) + bh * Nbp * D;
     const bf16* vbp = reinterpret_cast<const bf16*>(a.vbarP) + bh * Nbp * D;
     const int tail = (int)(N - (Nb - 1) * 64);  // keys in the last block (1..64)
+    srow[zero_bias + lane] = 0.f;
+    srow[tail_bias + lane] = lane < tail ? 0.f : -__builtin_inff();
 
     // Q^T as the B operand of S^T = K Q^T, parked in LDS in operand order:
     // 16-byte slot (nt*KS + s)*64 + lane holds query 32*nt + l32,
@@ -118,179 +243,63 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     }
     __syncthreads();
 
-    f32x16 oacc[MT][2];
+    RowState<D> rs;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) oacc[mt][nt][v] = 0.f;
-    float mref[2] = {-__builtin_inff(), -__builtin_inff()};
-    float lsum[2] = {0.f, 0.f};
+            for (int v = 0; v < 16; ++v) rs.oacc[mt][nt][v] = 0.f;
+    rs.mref[0] = rs.mref[1] = -__builtin_inff();
+    rs.lsum[0] = rs.lsum[1] = 0.f;
     const float scale2 = kLog2e / sqrtf((float)D);
-    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-    // Sequence of halves: exact tiles in kept-list order, then the pooled
-    // tiles holding a skipped block in ascending order.  An exact tail tile of
-    // <= 32 keys has only its first half.
+    // Tile sequence: exact blocks in kept-list order, then the pooled tiles
+    // holding a skipped block in ascending order.  Each tile is two 32-key
+    // halves (an exact tail block keeps its zero-padded keys masked).
+    // pm: pooled tiles not yet consumed as the current tile.
     const int n_tiles = n_kept + __popcll(tile_mask);
+    uint64_t pm = tile_mask;
     // (the kept-list entry is wave-uniform: readfirstlane keeps the tile
     // pointers in scalar registers)
-    auto exact_block = [&](int t) -> int64_t {
-        return (a.mode == kSparse) ? (int64_t)__builtin_amdgcn_readfirstlane((int)klist[t])
-                                   : (int64_t)t;
-    };
-    auto half_at = [&](int t, int u, int T) -> Half {
-        Half h;
-        h.u = u;
+    auto tile_at = [&](int t, uint64_t pmask) -> TileRef {
+        TileRef r;
         if (t < n_kept) {
-            const int64_t j = exact_block(t);
-            const int nv = ((j == Nb - 1) ? tail : 64) - 32 * u;
-            h.ktile = kp + j * (int64_t)D * 64;
-            h.vtile = vp + j * (int64_t)D * 64;
-            h.kind = nv < 32 ? 1 : 0;
-            h.nvalid = nv;
-            h.bias_off = 0;
+            const int64_t j = (a.mode == kSparse)
+                                  ? (int64_t)__builtin_amdgcn_readfirstlane((int)klist[t])
+                                  : (int64_t)t;
+            r.ktile = kp + j * (int64_t)D * 64;
+            r.vtile = vp + j * (int64_t)D * 64;
+            r.nvalid = (j == Nb - 1) ? tail : 64;
+            r.bias_off = r.nvalid < 64 ? tail_bias : zero_bias;
         } else {
-            h.ktile = kbp + (int64_t)T * D * 64;
-            h.vtile = vbp + (int64_t)T * D * 64;
-            h.kind = 2;
-            h.nvalid = 32;
-            h.bias_off = 64 * T + 32 * u;
+            const int T = __builtin_ctzll(pmask);
+            r.ktile = kbp + (int64_t)T * D * 64;
+            r.vtile = vbp + (int64_t)T * D * 64;
+            r.nvalid = 64;
+            r.bias_off = 64 * T;
         }
-        return h;
-    };
-    auto halves_of = [&](int t) -> int {
-        return (t < n_kept && exact_block(t) == Nb - 1 && tail <= 32) ? 1 : 2;
+        return r;
     };
 
-    uint64_t ptm = tile_mask;  // pooled tiles not yet finished
-    int t = 0, u = 0, pT = ptm ? __builtin_ctzll(ptm) : 0;
-    bf16x8 kA[KS];
-    bf16x8 vA[MT][2];
-    Half h = half_at(0, 0, pT);
-    load_k<D>(h, lane, kA);
+    bf16x8 kA0[KS], kA1[KS];
+    bf16x8 vA0[MT][2], vA1[MT][2];
+    TileRef cur = tile_at(0, pm);
+    load_k<D>(cur, 0, lane, kA0);
+    load_k<D>(cur, 1, lane, kA1);
+    load_v<D>(cur, 0, lane, vA0);
 
-    while (t < n_tiles) {
-        // which half comes next
-        int tn = t, un = u + 1, pTn = pT;
-        if (un >= halves_of(t)) {
-            tn = t + 1;
-            un = 0;
-            if (t >= n_kept) {  // leaving pooled tile pT
-                ptm &= ptm - 1;
-                pTn = ptm ? __builtin_ctzll(ptm) : 0;
-            }
-        }
-        const bool more = tn < n_tiles;
-        const Half hn = more ? half_at(tn, un, pTn) : h;
-
+    for (int t = 0; t < n_tiles; ++t) {
+        const bool more = t + 1 < n_tiles;
+        // next tile: when the current one is pooled, the next pooled tile is
+        // the following set bit of pm
+        const uint64_t pnext = (t >= n_kept) ? (pm & (pm - 1)) : pm;
+        const TileRef nxt = more ? tile_at(t + 1, pnext) : cur;
         // keep the Q operand reads inside the loop (no hoisting into VGPRs)
         __asm__ volatile("" ::: "memory");
-        // S^T = K Q^T: 32 keys x 64 queries, two 32x32 accumulators
-        f32x16 st[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) st[nt][v] = 0.f;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const bf16x8 q0 = qs[s * 64 + lane];
-            const bf16x8 q1 = qs[(KS + s) * 64 + lane];
-            st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[s], q0, st[0], 0, 0, 0);
-            st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[s], q1, st[1], 0, 0, 0);
-        }
-        // this half's values, needed after the softmax (the scheduling barrier
-        // keeps the loads behind the S^T products)
-        __builtin_amdgcn_sched_barrier(0);
-        load_v<D>(h, lane, vA);
-
-        // Logits in log2 units are st * sc (+ bias).  Pooled halves add the
-        // per-key bias log2(n_j) / -inf here (sc becomes 1); the exact tail
-        // masks keys past the block; exact halves keep the raw scores and
-        // fold the scale into the exp2 argument.  Register v holds key
-        // 8*(v/4) + 4*half + v%4 of this half.
-        float sc = scale2;
-        if (h.kind == 2) {
-            const float* b = srow + h.bias_off + 4 * half;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 bb = *reinterpret_cast<const f32x4*>(b + 8 * g);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-                        st[nt][4 * g + r] = st[nt][4 * g + r] * scale2 + bb[r];
-            }
-            sc = 1.0f;
-        } else if (h.kind == 1) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = 8 * (v >> 2) + 4 * half + (v & 3);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    if (key >= h.nvalid) st[nt][v] = -__builtin_inff();
-            }
-        }
-
-        // online softmax of both query halves -> P^T (bf16), the B operand of
-        // the PV product: k-step s holds keys 16*s + 4*half + {0..3, 8..11} of
-        // this half = accumulator registers 8*s .. 8*s+7
-        bf16x8 pB[2][2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            float mx = fmaxf(st[nt][0], st[nt][1]);
-#pragma unroll
-            for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(st[nt][v], st[nt][v + 1]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc;
-            const float mcand = fmaxf(mref[nt], mx);
-            const bool grow = mcand > mref[nt] + kRescaleSlack;
-            if (__ballot(grow)) {
-                const float mnew = grow ? mcand : mref[nt];
-                const float alpha = __builtin_amdgcn_exp2f(mref[nt] - mnew);
-                lsum[nt] *= alpha;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) oacc[mt][nt][v] *= alpha;
-                mref[nt] = mnew;
-            }
-            // (A pooled half whose keys are all kept blocks has only -inf
-            // logits; while no finite logit has been seen, subtract 0 so that
-            // such a half yields p = 0 rather than exp2(-inf + inf).)
-            const float msub = mref[nt] == -__builtin_inff() ? 0.f : mref[nt];
-            float ps = lsum[nt];
-#pragma unroll
-            for (int v = 0; v < 16; v += 2) {
-                f32x2 pp;
-                pp[0] = __builtin_amdgcn_exp2f(st[nt][v] * sc - msub);
-                pp[1] = __builtin_amdgcn_exp2f(st[nt][v + 1] * sc - msub);
-                const bf16x2 pr = __builtin_convertvector(pp, bf16x2);
-                ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
-                pB[nt][v >> 3][v & 7] = pr[0];
-                pB[nt][v >> 3][(v & 7) + 1] = pr[1];
-            }
-            lsum[nt] = ps;
-        }
-
-        // the K registers are free: fetch the next half's keys while the PV
-        // products run
-        __builtin_amdgcn_sched_barrier(0);
-        if (more) load_k<D>(hn, lane, kA);
-
-        // O^T += V^T P^T
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    oacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vA[mt][s], pB[nt][s],
-                                                                           oacc[mt][nt], 0, 0, 0);
-        h = hn;
-        t = tn;
-        u = un;
-        pT = pTn;
+        tile_step<D>(cur, nxt, more, qs, srow, lane, half, scale2, kA0, kA1, vA0, vA1, rs);
+        pm = pnext;
+        cur = nxt;
     }
 
     // epilogue: O = acc / l, rounded to bf16; lane holds query 32*nt + l32 and
@@ -298,7 +307,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     bf16* op = reinterpret_cast<bf16*>(a.out) + bh * N * D;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-        const float l = lsum[nt] + __shfl_xor(lsum[nt], 32, 64);
+        const float l = rs.lsum[nt] + __shfl_xor(rs.lsum[nt], 32, 64);
         const float inv = 1.0f / l;
         const int64_t row = i * 64 + 32 * nt + l32;
         if (row < N) {
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
                 for (int g = 0; g < 4; ++g) {
                     bf16x4 o;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] = to_bf16(oacc[mt][nt][4 * g + r] * inv);
+                    for (int r = 0; r < 4; ++r) o[r] = to_bf16(rs.oacc[mt][nt][4 * g + r] * inv);
                     *reinterpret_cast<bf16x4*>(op + row * D + 32 * mt + 8 * g + 4 * half) = o;
                 }
         }
@@ -316,7 +325,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-    const size_t lds = sizeof(float) * (a.Nbp + (a.Nb + 15) / 16 * 8) + 2 * 64 * (size_t)a.d;
+    const size_t lds = sizeof(float) * (a.Nbp + 128 + (a.Nb + 15) / 16 * 8) + 2 * 64 * (size_t)a.d;
     const dim3 grid((unsigned)(a.BH * a.Nb));
     if (a.d == 128)
         hipLaunchKernelGGL((attn_bf16_kernel<128>), grid, dim3(64), lds, s, a);
