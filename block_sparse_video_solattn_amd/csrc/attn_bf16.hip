@@ -10,14 +10,16 @@
 //     all 64 rows in one wave gives every K/V element loaded into registers
 //     64 rows of reuse;
 //   * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 with
-//     fp32 accumulation.  Q^T is parked in LDS in operand order.  Key and
+//     fp32 accumulation.  Q^T stays in registers.  Key and
 //     value tiles come pre-arranged in A-operand order from the pooling pass,
 //     so every operand load reads a contiguous 1 KiB run, and P^T is the S^T
 //     accumulator converted to bf16 with no lane shuffles;
-//   * each 64-key tile is consumed as two 32-key halves; a half's values are
-//     fetched behind its S^T products and the next half's keys behind its
-//     softmax, so keys and values are never live at once next to the 64 x d
-//     fp32 output accumulator;
+//   * each 64-key tile is consumed as two 32-key halves in a software
+//     pipeline: the S^T products of the next half are issued before the
+//     exp2 work of the current one, keys are fetched two halves ahead and
+//     values one half ahead into register double buffers.  One wave per
+//     SIMD leaves the whole register file (arch + accumulation VGPRs) to
+//     the 64 x d fp32 output accumulator, Q^T and these buffers;
 //   * skipped blocks enter as "pooled tiles": 64 pooled keys kbar_j (bf16)
 //     with logit bias log2(n_j), or -inf where block j is kept or padding.
 //     The pooled term n_j exp(c q.kbar_j) vbar_j is exactly a softmax column
@@ -74,62 +76,46 @@ struct RowState {
     float lsum[2];           // this lane's share of the denominator per query half
 };
 
-// One 32-key half u of tile `cur`: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// Right after the S^T products it issues the prefetches: the same half of the
-// next tile into kA, and the value operands the next half needs into vNext
-// (half 1 of this tile when u = 0, half 0 of the next tile when u = 1).
+// S^T = K Q^T for one 32-key half: 32 keys x 64 queries, two 32x32
+// accumulators (queries 0..31 and 32..63); Q^T held in registers.
 template <int D>
-__device__ __forceinline__ void half_step(int u, const TileRef& cur, const TileRef& nxt, bool more,
-                                          const bf16x8* __restrict__ qs, const float* srow,
-                                          int lane, int half, float scale2,
-                                          bf16x8 (&kA)[D / 16], bf16x8 (&vUse)[D / 32][2],
-                                          bf16x8 (&vNext)[D / 32][2], RowState<D>& rs) {
+__device__ __forceinline__ void s_product(const bf16x8 (&kA)[D / 16],
+                                          const bf16x8 (&qB)[2][D / 16], f32x16 (&st)[2]) {
     constexpr int KS = D / 16;
-    constexpr int MT = D / 32;
-    // S^T: 32 keys x 64 queries, two 32x32 accumulators; Q^T from LDS
-    f32x16 st[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) st[nt][v] = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        const bf16x8 q0 = qs[s * 64 + lane];
-        const bf16x8 q1 = qs[(KS + s) * 64 + lane];
-        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[s], q0, st[0], 0, 0, 0);
-        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[s], q1, st[1], 0, 0, 0);
+        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[s], qB[0][s], st[0], 0, 0, 0);
+        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[s], qB[1][s], st[1], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) load_k<D>(nxt, u, lane, kA);
-    if (u == 0)
-        load_v<D>(cur, 1, lane, vNext);
-    else if (more)
-        load_v<D>(nxt, 0, lane, vNext);
+}
 
+// Softmax, first part, for half u of tile `cur`: logits in log2 units with
+// the per-key bias, row maxima, and the (rare) rescale of the accumulators.
+// Returns in msub the reference each query half subtracts before exp2.
+template <int D>
+__device__ __forceinline__ void softmax_head(f32x16 (&st)[2], const TileRef& cur, int u,
+                                             const float* srow, int half, float scale2,
+                                             RowState<D>& rs, float (&msub)[2]) {
+    constexpr int MT = D / 32;
     // Logits in log2 units: st * scale2 + bias, with the per-key bias read
     // from LDS for every tile: 0 for exact keys, -inf for the zero-padded
     // keys past an exact tail block, log2(n_j) / -inf for pooled keys (kept
     // blocks and padding masked).  Register v of an accumulator holds key
     // 32*u + 8*(v/4) + 4*half + v%4 of the tile.
-    {
-        const float* b = srow + cur.bias_off + 32 * u + 4 * half;
+    const float* b = srow + cur.bias_off + 32 * u + 4 * half;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x4 bb = *reinterpret_cast<const f32x4*>(b + 8 * g);
+    for (int g = 0; g < 4; ++g) {
+        const f32x4 bb = *reinterpret_cast<const f32x4*>(b + 8 * g);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    st[nt][4 * g + r] = st[nt][4 * g + r] * scale2 + bb[r];
-        }
+            for (int nt = 0; nt < 2; ++nt)
+                st[nt][4 * g + r] = st[nt][4 * g + r] * scale2 + bb[r];
     }
-
-    // online softmax of both query halves -> P^T (bf16), the B operand of the
-    // PV product: k-step s holds keys 16*s + 4*half + {0..3, 8..11} of this
-    // half = accumulator registers 8*s .. 8*s+7.  The denominator adds the
-    // bf16-rounded weights the MFMA consumes (v_dot2 against (1, 1)).
-    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-    bf16x8 pB[2][2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         float mx = fmaxf(st[nt][0], st[nt][1]);
@@ -151,13 +137,26 @@ __device__ __forceinline__ void half_step(int u, const TileRef& cur, const TileR
         // (while no finite logit has been seen -- a pooled or tail half whose
         // keys are all masked -- subtract 0 so the half yields p = 0 rather
         // than exp2(-inf + inf))
-        const float msub = rs.mref[nt] == -__builtin_inff() ? 0.f : rs.mref[nt];
+        msub[nt] = rs.mref[nt] == -__builtin_inff() ? 0.f : rs.mref[nt];
+    }
+}
+
+// Softmax, second part: P^T in bf16 (the B operand of the PV product: k-step
+// s holds keys 16*s + 4*half + {0..3, 8..11} of the half = accumulator
+// registers 8*s .. 8*s+7) and the denominators, which add the bf16-rounded
+// weights the MFMA consumes (v_dot2 against (1, 1)).
+template <int D>
+__device__ __forceinline__ void softmax_tail(const f32x16 (&st)[2], const float (&msub)[2],
+                                             RowState<D>& rs, bf16x8 (&pB)[2][2]) {
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
         float ps = rs.lsum[nt];
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
             f32x2 pp;
-            pp[0] = __builtin_amdgcn_exp2f(st[nt][v] - msub);
-            pp[1] = __builtin_amdgcn_exp2f(st[nt][v + 1] - msub);
+            pp[0] = __builtin_amdgcn_exp2f(st[nt][v] - msub[nt]);
+            pp[1] = __builtin_amdgcn_exp2f(st[nt][v + 1] - msub[nt]);
             const bf16x2 pr = __builtin_convertvector(pp, bf16x2);
             ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
             pB[nt][v >> 3][v & 7] = pr[0];
@@ -165,27 +164,20 @@ __device__ __forceinline__ void half_step(int u, const TileRef& cur, const TileR
         }
         rs.lsum[nt] = ps;
     }
+}
 
-    // O^T += V^T P^T
+// O^T += V^T P^T for one half.
+template <int D>
+__device__ __forceinline__ void pv_product(const bf16x8 (&vA)[D / 32][2], const bf16x8 (&pB)[2][2],
+                                           RowState<D>& rs) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
-                rs.oacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vUse[mt][s], pB[nt][s],
+                rs.oacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vA[mt][s], pB[nt][s],
                                                                           rs.oacc[mt][nt], 0, 0, 0);
-}
-
-template <int D>
-__device__ __forceinline__ void tile_step(const TileRef& cur, const TileRef& nxt, bool more,
-                                          const bf16x8* __restrict__ qs, const float* srow,
-                                          int lane, int half, float scale2,
-                                          bf16x8 (&kA0)[D / 16], bf16x8 (&kA1)[D / 16],
-                                          bf16x8 (&vA0)[D / 32][2], bf16x8 (&vA1)[D / 32][2],
-                                          RowState<D>& rs) {
-    half_step<D>(0, cur, nxt, more, qs, srow, lane, half, scale2, kA0, vA0, vA1, rs);
-    half_step<D>(1, cur, nxt, more, qs, srow, lane, half, scale2, kA1, vA1, vA0, rs);
 }
 
 }  // namespace
@@ -202,11 +194,11 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     const int64_t bh = w / Nb, i = w % Nb;
     // LDS: srow[Nbp] routing scores, then pooled-key biases; two 64-entry
     // bias rows for exact tiles (all zero; zero then -inf past the tail
-    // block's last key); the kept list; Q^T in operand order
+    // block's last key); the kept list; the pooled-tile list
     float* srow = smem;
     const int zero_bias = (int)Nbp, tail_bias = (int)Nbp + 64;
     uint16_t* klist = reinterpret_cast<uint16_t*>(smem + Nbp + 128);
-    bf16x8* qs = reinterpret_cast<bf16x8*>(smem + Nbp + 128 + (Nb + 15) / 16 * 8);
+    uint16_t* plist = reinterpret_cast<uint16_t*>(smem + Nbp + 128 + (Nb + 15) / 16 * 8);
 
     int n_kept;
     uint64_t tile_mask;
@@ -229,17 +221,16 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     srow[zero_bias + lane] = 0.f;
     srow[tail_bias + lane] = lane < tail ? 0.f : -__builtin_inff();
 
-    // Q^T as the B operand of S^T = K Q^T, parked in LDS in operand order:
-    // 16-byte slot (nt*KS + s)*64 + lane holds query 32*nt + l32,
-    // d = 16*s + 8*half .. +7; read back with conflict-free ds_read_b128.
+    // Q^T as the B operand of S^T = K Q^T, held in registers for the whole
+    // query block: lane holds query 32*nt + l32, d = 16*s + 8*half .. +7
+    bf16x8 qB[2][KS];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         int64_t row = i * 64 + 32 * nt + l32;
         if (row > N - 1) row = N - 1;
         const bf16* qrow = qp + row * D + 8 * half;
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            qs[(nt * KS + s) * 64 + lane] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+        for (int s = 0; s < KS; ++s) qB[nt][s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
     }
     __syncthreads();
 
@@ -255,14 +246,14 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     const float scale2 = kLog2e / sqrtf((float)D);
 
     // Tile sequence: exact blocks in kept-list order, then the pooled tiles
-    // holding a skipped block in ascending order.  Each tile is two 32-key
-    // halves (an exact tail block keeps its zero-padded keys masked).
-    // pm: pooled tiles not yet consumed as the current tile.
+    // holding a skipped block in ascending order (plist).  Each tile is two
+    // 32-key halves (an exact tail block keeps its zero-padded keys masked).
     const int n_tiles = n_kept + __popcll(tile_mask);
-    uint64_t pm = tile_mask;
-    // (the kept-list entry is wave-uniform: readfirstlane keeps the tile
-    // pointers in scalar registers)
-    auto tile_at = [&](int t, uint64_t pmask) -> TileRef {
+    if (tile_mask >> lane & 1) plist[__popcll(tile_mask & ((1ull << lane) - 1))] = (uint16_t)lane;
+    __syncthreads();
+    // (list entries are wave-uniform: readfirstlane keeps the tile pointers in
+    // scalar registers)
+    auto tile_at = [&](int t) -> TileRef {
         TileRef r;
         if (t < n_kept) {
             const int64_t j = (a.mode == kSparse)
@@ -273,7 +264,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
             r.nvalid = (j == Nb - 1) ? tail : 64;
             r.bias_off = r.nvalid < 64 ? tail_bias : zero_bias;
         } else {
-            const int T = __builtin_ctzll(pmask);
+            const int T = __builtin_amdgcn_readfirstlane((int)plist[t - n_kept]);
             r.ktile = kbp + (int64_t)T * D * 64;
             r.vtile = vbp + (int64_t)T * D * 64;
             r.nvalid = 64;
@@ -282,24 +273,44 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
         return r;
     };
 
-    bf16x8 kA0[KS], kA1[KS];
-    bf16x8 vA0[MT][2], vA1[MT][2];
-    TileRef cur = tile_at(0, pm);
-    load_k<D>(cur, 0, lane, kA0);
-    load_k<D>(cur, 1, lane, kA1);
-    load_v<D>(cur, 0, lane, vA0);
+    // Software pipeline over halves h = (tile, u): the S^T products of half
+    // h+1 are issued before the exp2 work of half h, so the matrix cores and
+    // the vector ALU can run side by side; keys are fetched two
+    // halves ahead and values one half ahead, into two register buffers each
+    // (buffer = u).  Past the end the prefetches re-read the last tile, so
+    // every half runs the same straight-line code.
+    bf16x8 kB0[KS], kB1[KS];
+    bf16x8 vB0[MT][2], vB1[MT][2];
+    f32x16 st0[2], st1[2];
+    bf16x8 pB[2][2];
+    float msub[2];
+    TileRef t0 = tile_at(0);
+    TileRef t1 = n_tiles > 1 ? tile_at(1) : t0;
+    load_k<D>(t0, 0, lane, kB0);
+    load_k<D>(t0, 1, lane, kB1);
+    load_v<D>(t0, 0, lane, vB0);
+    s_product<D>(kB0, qB, st0);
+    load_k<D>(t1, 0, lane, kB0);
 
     for (int t = 0; t < n_tiles; ++t) {
-        const bool more = t + 1 < n_tiles;
-        // next tile: when the current one is pooled, the next pooled tile is
-        // the following set bit of pm
-        const uint64_t pnext = (t >= n_kept) ? (pm & (pm - 1)) : pm;
-        const TileRef nxt = more ? tile_at(t + 1, pnext) : cur;
-        // keep the Q operand reads inside the loop (no hoisting into VGPRs)
-        __asm__ volatile("" ::: "memory");
-        tile_step<D>(cur, nxt, more, qs, srow, lane, half, scale2, kA0, kA1, vA0, vA1, rs);
-        pm = pnext;
-        cur = nxt;
+        const TileRef t2 = t + 2 < n_tiles ? tile_at(t + 2) : t1;
+        // half (t, 0): softmax head of (t, 0); S^T of (t, 1) with the softmax
+        // tail of (t, 0); PV of (t, 0)
+        softmax_head<D>(st0, t0, 0, srow, half, scale2, rs, msub);
+        s_product<D>(kB1, qB, st1);
+        load_k<D>(t1, 1, lane, kB1);
+        load_v<D>(t0, 1, lane, vB1);
+        softmax_tail<D>(st0, msub, rs, pB);
+        pv_product<D>(vB0, pB, rs);
+        // half (t, 1): the same with S^T of (t+1, 0)
+        softmax_head<D>(st1, t0, 1, srow, half, scale2, rs, msub);
+        s_product<D>(kB0, qB, st0);
+        load_k<D>(t2, 0, lane, kB0);
+        load_v<D>(t1, 0, lane, vB0);
+        softmax_tail<D>(st1, msub, rs, pB);
+        pv_product<D>(vB1, pB, rs);
+        t0 = t1;
+        t1 = t2;
     }
 
     // epilogue: O = acc / l, rounded to bf16; lane holds query 32*nt + l32 and
@@ -325,7 +336,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-    const size_t lds = sizeof(float) * (a.Nbp + 128 + (a.Nb + 15) / 16 * 8) + 2 * 64 * (size_t)a.d;
+    const size_t lds = sizeof(float) * (a.Nbp + 128 + (a.Nb + 15) / 16 * 8 + 32);
     const dim3 grid((unsigned)(a.BH * a.Nb));
     if (a.d == 128)
         hipLaunchKernelGGL((attn_bf16_kernel<128>), grid, dim3(64), lds, s, a);
