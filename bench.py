@@ -22,6 +22,35 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
 SEED = 3000
 
+# HBM traffic of one attention dispatch from rocprofv3 counters on this
+# workload: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), scaled by what the
+# same counters read for plain copies of known size in the same runs (x2 for
+# FETCH_SIZE, x1 for WRITE_SIZE).  The figures belong to the kernel sources
+# they were measured on; after any change to those sources the traffic is
+# reported as null until the counters are taken again.
+ATTN_COUNTERS = {
+    "sources_sha256": "dd8034ee67972a8cb94990672355e37707f0dc1847222763b625be27091401b4",
+    "fetch_kib": 744444.6, "fetch_scale": 2.0,
+    "write_kib": 131077.0, "write_scale": 1.0,
+}
+ATTN_SOURCES = ("attn_bf16.hip", "route.h", "common.h", "launch.h")
+
+
+def attn_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for name in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_video_solattn_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def attn_traffic_bytes():
+    c = ATTN_COUNTERS
+    if attn_sources_sha256() != c["sources_sha256"]:
+        return None
+    return int(round((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024))
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -181,7 +210,7 @@ def main():
         "pooled_tflop": round(fp / 1e12, 5),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "attn_bf16_kernel<128>"},
+                     "traffic": attn_traffic_bytes(), "kernel": "attn_bf16_kernel<128>"},
     }
 
     if not args.no_extra:
