@@ -8,7 +8,8 @@ generators in ``.inputs`` need no library.
 _BINDING_NAMES = (
     "BF16", "DENSE", "EXPORTS", "F32", "SPARSE", "SolAttnError", "solattn_attend_ws",
     "solattn_forward", "solattn_forward_debug", "solattn_forward_ws", "solattn_last_error",
-    "solattn_pool", "solattn_prepare_ws", "solattn_route", "solattn_strerror",
+    "solattn_pool", "solattn_prepare_ws", "solattn_probe_mfma_bf16", "solattn_route",
+    "solattn_strerror",
     "solattn_version", "solattn_workspace_bytes", "unpack_mask", "raw_call",
 )
 

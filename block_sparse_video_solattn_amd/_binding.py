@@ -49,6 +49,7 @@ _SIGS = {
     "solattn_forward_debug": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P, _P, _P, _P], _I),
     "solattn_pool": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P], _I),
     "solattn_route": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _P, _P, _P, _P], _I),
+    "solattn_probe_mfma_bf16": ([_P, _I64, _I64, _P], _I),
     "solattn_strerror": ([_I], ctypes.c_char_p),
     "solattn_last_error": ([], ctypes.c_char_p),
     "solattn_version": ([], ctypes.c_char_p),
@@ -223,6 +224,14 @@ def solattn_route(q, k, v, prefix_len: int, tau: float, stream=None, want_scores
     _check(_lib.solattn_route(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, prefix_len, float(tau),
                               _dtype_code(q), _ptr(mask), _ptr(scores), _ptr(thr), _stream(stream)))
     return mask, scores, thr
+
+
+def solattn_probe_mfma_bf16(sink, waves: int, iters: int, stream=None):
+    """Enqueue the bf16 MFMA peak probe (waves * iters * 16 * 32768 FLOP);
+    sink: float32 device tensor of at least waves * 64 elements."""
+    if sink.numel() < waves * 64:
+        raise ValueError("sink needs waves * 64 floats")
+    _check(_lib.solattn_probe_mfma_bf16(_ptr(sink), int(waves), int(iters), _stream(stream)))
 
 
 def raw_call(name: str, *args) -> int:

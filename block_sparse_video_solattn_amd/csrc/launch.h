@@ -92,4 +92,7 @@ hipError_t launch_route(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
+// bf16 MFMA peak probe: `waves` wavefronts x `iters` x 16 MFMAs 32x32x16.
+hipError_t launch_probe_mfma(float* sink, int64_t waves, int64_t iters, hipStream_t s);
+
 }  // namespace solattn

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/solattn.h"
+#include "../../include/solattn_probe.h"
 #include "launch.h"
 
 using namespace solattn;
@@ -300,6 +301,19 @@ const char* solattn_strerror(int code) {
 }
 
 const char* solattn_last_error(void) { return g_last_error.c_str(); }
+
+int solattn_probe_mfma_bf16(float* sink, int64_t waves, int64_t iters, void* stream) {
+    g_last_error.clear();
+    if (!sink) return fail(SOLATTN_EINVAL, "sink must be non-NULL");
+    if (!aligned16(sink)) return fail(SOLATTN_EINVAL, "sink must be 16-byte aligned");
+    if (waves < 1 || waves > (1LL << 20))
+        return fail(SOLATTN_EINVAL, "waves must be in [1, 2^20] (got %lld)", (long long)waves);
+    if (iters < 1 || iters > (1LL << 20))
+        return fail(SOLATTN_EINVAL, "iters must be in [1, 2^20] (got %lld)", (long long)iters);
+    const hipError_t e = launch_probe_mfma(sink, waves, iters, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "probe launch");
+    return SOLATTN_OK;
+}
 
 const char* solattn_version(void) { return "solattn-mi355x 0.1.0 (gfx950)"; }
 

@@ -2,6 +2,7 @@
 include/solattn.h declares, and rejects bad arguments on the host before any
 device call."""
 import ctypes
+import glob
 import math
 import os
 import re
@@ -10,13 +11,15 @@ import pytest
 
 from conftest import ROOT, ensure_library
 
-HEADER = os.path.join(ROOT, "include", "solattn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(solattn_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(solattn_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -101,3 +104,14 @@ def test_import_without_library_fails_loudly(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                        cwd=str(tmp_path))
     assert r.returncode != 0 and "not built" in r.stderr
+
+
+def test_probe_rejects_bad_arguments_on_host(lib):
+    probe = lambda sink, waves, iters: lib.raw_call("solattn_probe_mfma_bf16", sink, waves, iters, None)
+    assert probe(None, 1024, 16) == lib.EINVAL
+    assert "sink" in lib.solattn_last_error()
+    assert probe(A + 4, 1024, 16) == lib.EINVAL  # misaligned
+    assert probe(A, 0, 16) == lib.EINVAL
+    assert probe(A, (1 << 20) + 1, 16) == lib.EINVAL
+    assert probe(A, 1024, 0) == lib.EINVAL
+    assert "iters" in lib.solattn_last_error()
