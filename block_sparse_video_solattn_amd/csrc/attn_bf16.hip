@@ -15,21 +15,28 @@
 //     so every operand load reads a contiguous 1 KiB run, and P^T is the S^T
 //     accumulator converted to bf16 with no lane shuffles;
 //   * each 64-key tile is consumed as two 32-key halves in a software
-//     pipeline: the S^T products of the next half are issued before the
-//     exp2 work of the current one, keys are fetched two halves ahead and
-//     values one half ahead into register double buffers.  One wave per
-//     SIMD leaves the whole register file (arch + accumulation VGPRs) to
-//     the 64 x d fp32 output accumulator, Q^T and these buffers;
+//     pipeline whose phases pair matrix-core and vector work: the S^T
+//     products of half h+1 run beside the exp2 work of half h, and the PV
+//     products of half h beside the logits and maxima of half h+1, with
+//     the MFMAs and vector instructions interleaved one by one.  Keys are
+//     prefetched into registers two halves ahead, values one half ahead;
+//   * one wave per SIMD: the 64 x d fp32 output accumulator and the value
+//     buffers live in the accumulation VGPRs (the PV MFMAs are inline asm),
+//     the arch VGPRs hold Q^T, S^T, P and the key buffers;
 //   * skipped blocks enter as "pooled tiles": 64 pooled keys kbar_j (bf16)
 //     with logit bias log2(n_j), or -inf where block j is kept or padding.
 //     The pooled term n_j exp(c q.kbar_j) vbar_j is exactly a softmax column
 //     with logit c q.kbar_j + ln n_j, so it shares the MFMA body and the
 //     online-softmax state with the exact tiles;
-//   * the online softmax runs in log2 units (exp2) with a lazy rescale: the
-//     reference maximum moves only when the row maximum grows by more than
-//     2^8, which keeps P <= 256 in bf16 and skips most rescales of the
-//     accumulators.  The denominator adds the bf16-rounded weights the MFMA
-//     consumes (v_dot2 against (1, 1)), so numerator and denominator agree;
+//   * the online softmax runs in log2 units (exp2).  The fast path fixes
+//     each row's reference at the maximum of its first half with a finite
+//     logit and never rescales: weights up to 2^64 above it stay far from
+//     the fp32/bf16 range limit.  If some row's maximum rose further, the
+//     fast path's result is discarded after its loop and the query block is
+//     recomputed from the start by the rescaling path (VGPR accumulators,
+//     lazy rescale when the maximum grows by more than 2^8).  The denominator adds the
+//     bf16-rounded weights the MFMA consumes (v_dot2 against (1, 1)), so
+//     numerator and denominator agree;
 //   * workgroups are remapped so that the query blocks of one head run on
 //     one XCD and share its L2 for the K/V tiles they keep.
 #include "common.h"
@@ -41,7 +48,8 @@ namespace solattn {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.0f;
+constexpr float kRescaleSlack = 8.0f;   // rescaling path: lazy-rescale margin (log2)
+constexpr float kFixedSlack = 64.0f;    // fast path: growth over the fixed reference (log2)
 
 // One 64-key tile of the sequence: an exact key block or a pooled tile.
 struct TileRef {
@@ -68,12 +76,55 @@ __device__ inline void load_v(const TileRef& t, int u, int lane, bf16x8 (&vA)[D 
             vA[mt][s] = *reinterpret_cast<const bf16x8*>(t.vtile + vtile_offset(mt, 2 * u + s, lane, 0));
 }
 
+// Scheduling pattern for one phase: N groups of one MFMA followed by up to
+// V vector-ALU instructions, so the wave issues softmax work while the
+// matrix core runs.
+template <int N, int V>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    }
+}
+
+// Wait states after the inline-asm PV MFMAs before any other instruction
+// touches their accumulation registers (or the registers are reused):
+// 8 x 16 wait states, several times the latency of a 16-pass MFMA.
+__device__ __forceinline__ void acc_fence() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile(
+        "s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15\n\t"
+        "s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// max(x, x of lane ^ 32) without an LDS round trip: v_permlane32_swap
+// exchanges the upper 32 lanes of one copy with the lower 32 lanes of the
+// other, so each lane ends up holding both values.
+__device__ __forceinline__ float max_across_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Shared state of one wave's 64 query rows.
 template <int D>
 struct RowState {
     f32x16 oacc[D / 32][2];  // O^T accumulators: d = 32*mt + ..., queries 32*nt + l32
     float mref[2];           // reference maximum (log2 units) per query half
     float lsum[2];           // this lane's share of the denominator per query half
+};
+
+// State of the fast path: the output accumulators are bound to
+// accumulation VGPRs by the inline-asm PV MFMAs; the reference maximum is
+// fixed once per row.
+template <int D>
+struct FixedState {
+    f32x16 oacc[D / 32][2];
+    float mref[2];
+    float lsum[2];
+    float growth[2];  // largest row maximum seen above the reference
 };
 
 // S^T = K Q^T for one 32-key half: 32 keys x 64 queries, two 32x32
@@ -141,13 +192,45 @@ __device__ __forceinline__ void softmax_head(f32x16 (&st)[2], const TileRef& cur
     }
 }
 
+// Fast-path softmax, first part: logits in log2 units with the per-key bias
+// (as in softmax_head), row maxima, and the fixed reference: set by the
+// first half whose row maximum is finite, never moved afterwards.  Tracks
+// how far later row maxima rise above it; past kFixedSlack the fast path's
+// results are discarded.
+template <int D>
+__device__ __forceinline__ void softmax_head_fixed(f32x16 (&st)[2], const TileRef& cur, int u,
+                                                   const float* srow, int half, float scale2,
+                                                   FixedState<D>& fs, float (&msub)[2]) {
+    const float* b = srow + cur.bias_off + 32 * u + 4 * half;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const f32x4 bb = *reinterpret_cast<const f32x4*>(b + 8 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                st[nt][4 * g + r] = st[nt][4 * g + r] * scale2 + bb[r];
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        float mx = fmaxf(st[nt][0], st[nt][1]);
+#pragma unroll
+        for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(st[nt][v], st[nt][v + 1]));
+        mx = max_across_halves(mx);
+        if (fs.mref[nt] == -__builtin_inff()) fs.mref[nt] = mx;
+        // (-inf - -inf is NaN, which fmaxf ignores)
+        fs.growth[nt] = fmaxf(fs.growth[nt], mx - fs.mref[nt]);
+        msub[nt] = fs.mref[nt] == -__builtin_inff() ? 0.f : fs.mref[nt];
+    }
+}
+
 // Softmax, second part: P^T in bf16 (the B operand of the PV product: k-step
 // s holds keys 16*s + 4*half + {0..3, 8..11} of the half = accumulator
 // registers 8*s .. 8*s+7) and the denominators, which add the bf16-rounded
 // weights the MFMA consumes (v_dot2 against (1, 1)).
-template <int D>
+template <typename State>
 __device__ __forceinline__ void softmax_tail(const f32x16 (&st)[2], const float (&msub)[2],
-                                             RowState<D>& rs, bf16x8 (&pB)[2][2]) {
+                                             State& rs, bf16x8 (&pB)[2][2]) {
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -180,7 +263,141 @@ __device__ __forceinline__ void pv_product(const bf16x8 (&vA)[D / 32][2], const 
                                                                           rs.oacc[mt][nt], 0, 0, 0);
 }
 
+// O^T += V^T P^T for one half on the fast path, with the output
+// accumulators in accumulation VGPRs: written as inline assembly so the
+// compiler keeps the 128 accumulator registers out of the arch VGPRs.  The
+// hazards the compiler would otherwise cover are handled here: the leading
+// s_nop gives the wait states a VALU write of P (the bf16 conversion)
+// needs before an MFMA reads it, and the k-step-major order puts 2*MT - 1
+// other MFMAs between two MFMAs that accumulate into the same registers.
+__device__ __forceinline__ void mfma_pv_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "a"(a), "v"(b));
+}
+
+template <int D>
+__device__ __forceinline__ void pv_product_acc(const bf16x8 (&vA)[D / 32][2],
+                                               const bf16x8 (&pB)[2][2], FixedState<D>& fs) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) mfma_pv_acc(fs.oacc[mt][nt], vA[mt][s], pB[nt][s]);
+}
+
+// O = acc / l rounded to bf16; lane holds query 32*nt + l32 and
+// d = 32*mt + 8*g + 4*half + r.
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16 (&oacc)[D / 32][2], const float (&lsum)[2],
+                                           bf16* op, int64_t i, int64_t N, int half, int l32) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const float l = lsum[nt] + __shfl_xor(lsum[nt], 32, 64);
+        const float inv = 1.0f / l;
+        const int64_t row = i * 64 + 32 * nt + l32;
+        if (row < N) {
+#pragma unroll
+            for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    bf16x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = to_bf16(oacc[mt][nt][4 * g + r] * inv);
+                    *reinterpret_cast<bf16x4*>(op + row * D + 32 * mt + 8 * g + 4 * half) = o;
+                }
+        }
+    }
+}
+
 }  // namespace
+
+// Rescaling path, for query blocks whose logits grow too far past the
+// first half's maximum: the block is recomputed from the start with a
+// moving reference (lazy rescale).  A separate, never-inlined function, so
+// that its register needs stay out of the fast path's allocation.  The S^T
+// products of half h+1 are issued before the exp2 work of half h; keys are
+// fetched two halves ahead and values one half ahead, into two register
+// buffers each (buffer = u).
+template <int D>
+__device__ __attribute__((noinline)) void attend_rescaling(
+    const bf16* qp, const bf16* kp, const bf16* vp, const bf16* kbp, const bf16* vbp, bf16* op,
+    int64_t N, int64_t Nb, int64_t Nbp, int sparse, int64_t i, int n_kept, uint64_t tile_mask,
+    const float* srow, const uint16_t* klist, const uint16_t* plist) {
+    constexpr int KS = D / 16;
+    constexpr int MT = D / 32;
+    const int lane = threadIdx.x, half = lane >> 5, l32 = lane & 31;
+    const int zero_bias = (int)Nbp, tail_bias = (int)Nbp + 64;
+    const int tail = (int)(N - (Nb - 1) * 64);
+    bf16x8 qB[2][KS];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        int64_t row = i * 64 + 32 * nt + l32;
+        if (row > N - 1) row = N - 1;
+        const bf16* qrow = qp + row * D + 8 * half;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qB[nt][s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+    }
+    const int n_tiles = n_kept + __popcll(tile_mask);
+    auto tile_at = [&](int t) -> TileRef {
+        TileRef r;
+        if (t < n_kept) {
+            const int64_t j = sparse ? (int64_t)__builtin_amdgcn_readfirstlane((int)klist[t])
+                                     : (int64_t)t;
+            r.ktile = kp + j * (int64_t)D * 64;
+            r.vtile = vp + j * (int64_t)D * 64;
+            r.nvalid = (j == Nb - 1) ? tail : 64;
+            r.bias_off = r.nvalid < 64 ? tail_bias : zero_bias;
+        } else {
+            const int T = __builtin_amdgcn_readfirstlane((int)plist[t - n_kept]);
+            r.ktile = kbp + (int64_t)T * D * 64;
+            r.vtile = vbp + (int64_t)T * D * 64;
+            r.nvalid = 64;
+            r.bias_off = 64 * T;
+        }
+        return r;
+    };
+    const float scale2 = kLog2e / sqrtf((float)D);
+    RowState<D> rs;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) rs.oacc[mt][nt][v] = 0.f;
+    rs.mref[0] = rs.mref[1] = -__builtin_inff();
+    rs.lsum[0] = rs.lsum[1] = 0.f;
+    bf16x8 kB0[KS], kB1[KS];
+    bf16x8 vB0[MT][2], vB1[MT][2];
+    f32x16 st0[2], st1[2];
+    bf16x8 pB[2][2];
+    float msub[2];
+    TileRef t0 = tile_at(0);
+    TileRef t1 = n_tiles > 1 ? tile_at(1) : t0;
+    load_k<D>(t0, 0, lane, kB0);
+    load_k<D>(t0, 1, lane, kB1);
+    load_v<D>(t0, 0, lane, vB0);
+    s_product<D>(kB0, qB, st0);
+    load_k<D>(t1, 0, lane, kB0);
+
+    for (int t = 0; t < n_tiles; ++t) {
+        const TileRef t2 = t + 2 < n_tiles ? tile_at(t + 2) : t1;
+        softmax_head<D>(st0, t0, 0, srow, half, scale2, rs, msub);
+        s_product<D>(kB1, qB, st1);
+        load_k<D>(t1, 1, lane, kB1);
+        load_v<D>(t0, 1, lane, vB1);
+        softmax_tail(st0, msub, rs, pB);
+        pv_product<D>(vB0, pB, rs);
+        softmax_head<D>(st1, t0, 1, srow, half, scale2, rs, msub);
+        s_product<D>(kB0, qB, st0);
+        load_k<D>(t2, 0, lane, kB0);
+        load_v<D>(t1, 0, lane, vB0);
+        softmax_tail(st1, msub, rs, pB);
+        pv_product<D>(vB1, pB, rs);
+        t0 = t1;
+        t1 = t2;
+    }
+    store_rows<D>(rs.oacc, rs.lsum, op, i, N, half, l32);
+}
 
 template <int D>
 __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
@@ -234,15 +451,6 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     }
     __syncthreads();
 
-    RowState<D> rs;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) rs.oacc[mt][nt][v] = 0.f;
-    rs.mref[0] = rs.mref[1] = -__builtin_inff();
-    rs.lsum[0] = rs.lsum[1] = 0.f;
     const float scale2 = kLog2e / sqrtf((float)D);
 
     // Tile sequence: exact blocks in kept-list order, then the pooled tiles
@@ -272,67 +480,92 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
         }
         return r;
     };
-
-    // Software pipeline over halves h = (tile, u): the S^T products of half
-    // h+1 are issued before the exp2 work of half h, so the matrix cores and
-    // the vector ALU can run side by side; keys are fetched two
-    // halves ahead and values one half ahead, into two register buffers each
-    // (buffer = u).  Past the end the prefetches re-read the last tile, so
-    // every half runs the same straight-line code.
-    bf16x8 kB0[KS], kB1[KS];
-    bf16x8 vB0[MT][2], vB1[MT][2];
-    f32x16 st0[2], st1[2];
-    bf16x8 pB[2][2];
-    float msub[2];
-    TileRef t0 = tile_at(0);
-    TileRef t1 = n_tiles > 1 ? tile_at(1) : t0;
-    load_k<D>(t0, 0, lane, kB0);
-    load_k<D>(t0, 1, lane, kB1);
-    load_v<D>(t0, 0, lane, vB0);
-    s_product<D>(kB0, qB, st0);
-    load_k<D>(t1, 0, lane, kB0);
-
-    for (int t = 0; t < n_tiles; ++t) {
-        const TileRef t2 = t + 2 < n_tiles ? tile_at(t + 2) : t1;
-        // half (t, 0): softmax head of (t, 0); S^T of (t, 1) with the softmax
-        // tail of (t, 0); PV of (t, 0)
-        softmax_head<D>(st0, t0, 0, srow, half, scale2, rs, msub);
-        s_product<D>(kB1, qB, st1);
-        load_k<D>(t1, 1, lane, kB1);
-        load_v<D>(t0, 1, lane, vB1);
-        softmax_tail<D>(st0, msub, rs, pB);
-        pv_product<D>(vB0, pB, rs);
-        // half (t, 1): the same with S^T of (t+1, 0)
-        softmax_head<D>(st1, t0, 1, srow, half, scale2, rs, msub);
-        s_product<D>(kB0, qB, st0);
-        load_k<D>(t2, 0, lane, kB0);
-        load_v<D>(t1, 0, lane, vB0);
-        softmax_tail<D>(st1, msub, rs, pB);
-        pv_product<D>(vB1, pB, rs);
-        t0 = t1;
-        t1 = t2;
-    }
-
-    // epilogue: O = acc / l, rounded to bf16; lane holds query 32*nt + l32 and
-    // d = 32*mt + 8*g + 4*half + r
     bf16* op = reinterpret_cast<bf16*>(a.out) + bh * N * D;
+
+    // Fast path.  Phases (sched barriers keep them, and so the order of the
+    // loads that the in-order vmcnt waits rely on, in place):
+    //   S^T of half h+1 beside the exp2 work of half h;
+    //   loads of the values of half h+1, then of the keys of half h+3;
+    //   PV of half h beside the logits, maxima and bias of half h+1.
+    // Past the end the prefetches and the S^T products re-read the last tile
+    // (their results are never used), so every iteration runs the same
+    // straight-line code; a repeated half cannot raise a row's maximum.
+    bool abandoned = false;
+    {
+        FixedState<D> fs;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const float l = rs.lsum[nt] + __shfl_xor(rs.lsum[nt], 32, 64);
-        const float inv = 1.0f / l;
-        const int64_t row = i * 64 + 32 * nt + l32;
-        if (row < N) {
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    bf16x4 o;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] = to_bf16(rs.oacc[mt][nt][4 * g + r] * inv);
-                    *reinterpret_cast<bf16x4*>(op + row * D + 32 * mt + 8 * g + 4 * half) = o;
-                }
+                for (int v = 0; v < 16; ++v) fs.oacc[mt][nt][v] = 0.f;
+        fs.mref[0] = fs.mref[1] = -__builtin_inff();
+        fs.lsum[0] = fs.lsum[1] = 0.f;
+        fs.growth[0] = fs.growth[1] = 0.f;
+        bf16x8 kB0[KS], kB1[KS];            // keys of even / odd halves
+        bf16x8 vB0[MT][2], vB1[MT][2];      // values (accumulation VGPRs)
+        f32x16 st0[2], st1[2];
+        bf16x8 pB[2][2];
+        float msub0[2], msub1[2];
+        TileRef t0 = tile_at(0);
+        TileRef t1 = n_tiles > 1 ? tile_at(1) : t0;
+        // (the loads outstanding when the loop is entered are issued in the
+        // order of the loop's own, so the wait counts at the loop head hold
+        // on both paths)
+        load_k<D>(t0, 0, lane, kB0);
+        s_product<D>(kB0, qB, st0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_k<D>(t0, 1, lane, kB1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_v<D>(t0, 0, lane, vB0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_k<D>(t1, 0, lane, kB0);
+        __builtin_amdgcn_sched_barrier(0);
+        softmax_head_fixed<D>(st0, t0, 0, srow, half, scale2, fs, msub0);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Keys are fetched two halves ahead, values one half ahead; a load
+        // phase issues the values first (they are needed first).
+        for (int t = 0; t < n_tiles; ++t) {
+            const TileRef t2 = t + 2 < n_tiles ? tile_at(t + 2) : t1;
+            s_product<D>(kB1, qB, st1);                      // S^T (t, 1)
+            softmax_tail(st0, msub0, fs, pB);                // exp2 (t, 0)
+            interleave<16, 6>();
+            __builtin_amdgcn_sched_barrier(0);
+            load_v<D>(t0, 1, lane, vB1);
+            __builtin_amdgcn_sched_barrier(0);
+            load_k<D>(t1, 1, lane, kB1);
+            __builtin_amdgcn_sched_barrier(0);
+            pv_product_acc<D>(vB0, pB, fs);                  // PV (t, 0)
+            softmax_head_fixed<D>(st1, t0, 1, srow, half, scale2, fs, msub1);
+            interleave<16, 4>();
+            __builtin_amdgcn_sched_barrier(0);
+            s_product<D>(kB0, qB, st0);                      // S^T (t+1, 0)
+            softmax_tail(st1, msub1, fs, pB);                // exp2 (t, 1)
+            interleave<16, 6>();
+            __builtin_amdgcn_sched_barrier(0);
+            load_v<D>(t1, 0, lane, vB0);
+            __builtin_amdgcn_sched_barrier(0);
+            load_k<D>(t2, 0, lane, kB0);
+            __builtin_amdgcn_sched_barrier(0);
+            pv_product_acc<D>(vB1, pB, fs);                  // PV (t, 1)
+            softmax_head_fixed<D>(st0, t1, 0, srow, half, scale2, fs, msub0);
+            interleave<16, 4>();
+            __builtin_amdgcn_sched_barrier(0);
+            t0 = t1;
+            t1 = t2;
         }
+        // (the loop runs to its end even when some row rose past its
+        // reference -- inf or NaN may then have reached the accumulators --
+        // and the results are discarded here)
+        abandoned = __ballot(fmaxf(fs.growth[0], fs.growth[1]) > kFixedSlack) != 0;
+        acc_fence();
+        if (!abandoned) store_rows<D>(fs.oacc, fs.lsum, op, i, N, half, l32);
     }
+    if (!abandoned) return;
+
+    attend_rescaling<D>(qp, kp, vp, kbp, vbp, op, N, Nb, Nbp, a.mode == kSparse, i, n_kept, tile_mask,
+                        srow, klist, plist);
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {

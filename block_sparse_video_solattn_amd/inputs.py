@@ -171,3 +171,30 @@ def custom(B, H, N, D, dtype="bf16", prefix_len=0, seed=0, kind="iid_qk_offset",
         grid = (1, 1, max(1, n_video))
     w = Workload("custom", B, H, N, D, dtype, prefix_len, (), grid, kind)
     return make_inputs(w, seed)
+
+
+def logit_jump(B, H, N, D, dtype="bf16", jump_block=5, scale=6.0, seed=0) -> tuple:
+    """Inputs whose logits rise steeply after the first key block: every
+    query row is a shared direction u (i.i.d. N(0,1) per head) plus N(0, 0.25^2)
+    noise; keys are i.i.d. N(0,1) except block ``jump_block``, whose rows are
+    scale * u plus N(0, 0.1^2) noise; values i.i.d. N(0,1).  Against that block
+    a query's logit is about scale * |u|^2 / sqrt(D) (natural units) while
+    block 0's logits stay of order one -- the case where a softmax reference
+    taken from the first block falls far below the row maximum."""
+    q = np.empty((B, H, N, D), np.float32)
+    k = np.empty((B, H, N, D), np.float32)
+    v = np.empty((B, H, N, D), np.float32)
+    lo, hi = jump_block * BLOCK, min(N, (jump_block + 1) * BLOCK)
+    for b in range(B):
+        for h in range(H):
+            rng = _rng(seed, b, h)
+            u = rng.standard_normal(D)
+            q[b, h] = u[None, :] + 0.25 * rng.standard_normal((N, D))
+            kk = rng.standard_normal((N, D))
+            kk[lo:hi] = scale * u[None, :] + 0.1 * rng.standard_normal((hi - lo, D))
+            k[b, h] = kk
+            v[b, h] = rng.standard_normal((N, D))
+    if dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    return q, k, v
+

@@ -194,6 +194,22 @@ def test_all_blocks_constant_tau_inf_equals_dense():
                     assert ab <= TOL_BF16_ABS, (name, ab)
 
 
+@pytest.mark.parametrize("mode", ["sparse", "dense"])
+@pytest.mark.parametrize("scale", [2.5, 10.0])
+def test_steep_logit_rise_after_first_block(mode, scale):
+    # Logits against key block 5 exceed block 0's (the first tile) by about
+    # 30 (scale 2.5) or 125..150 (scale 10) log2 units.  A softmax reference
+    # fixed at the first tile's maximum handles the first; the second would
+    # overflow bf16/fp32 weights (> 2^128), so the GPU must rescale there.
+    q, k, v = inputs.logit_jump(1, 2, 64 * 12 + 20, 128, "bf16", jump_block=5, scale=scale, seed=41)
+    check_forward(q, k, v, "bf16", 64, 1.25, mode)
+
+
+def test_steep_logit_rise_f32():
+    q, k, v = inputs.logit_jump(1, 1, 64 * 9 + 7, 64, "f32", jump_block=3, scale=10.0, seed=42)
+    check_forward(q, k, v, "f32", 64, 1.0)
+
+
 def test_pooled_only_path_f32():
     q, k, v = inputs.custom(1, 1, 1024, 64, "f32", seed=34)
     check_forward(q, k, v, "f32", 0, math.inf)
