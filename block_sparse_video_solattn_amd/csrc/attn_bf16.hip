@@ -274,15 +274,63 @@ __device__ __forceinline__ void mfma_pv_acc(f32x16& acc, const bf16x8& a, const 
     asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "a"(a), "v"(b));
 }
 
+// PV of one half on the fast path with the logits, maxima and reference
+// update of the next half (softmax_head_fixed's work) spread between its
+// MFMAs by hand: the asm MFMAs are invisible to the scheduler's grouping, so
+// the order is written out and pinned with scheduling barriers.  The work
+// is cut into 16 slices: bias terms 4 at a time (slices 0-7), then the row
+// maxima, the cross-half maxima and the reference update (8-15).
 template <int D>
-__device__ __forceinline__ void pv_product_acc(const bf16x8 (&vA)[D / 32][2],
-                                               const bf16x8 (&pB)[2][2], FixedState<D>& fs) {
+__device__ __forceinline__ void head_slice(int m, f32x16 (&st)[2], const f32x4 (&bb)[4],
+                                           float scale2, FixedState<D>& fs, float (&msub)[2],
+                                           float (&part)[2][2]) {
+    if (m < 8) {
+        const int g = m >> 1, nt = m & 1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[nt][4 * g + r] = st[nt][4 * g + r] * scale2 + bb[g][r];
+    } else if (m < 12) {
+        const int nt = (m - 8) >> 1, h8 = ((m - 8) & 1) * 8;
+        float mx = fmaxf(st[nt][h8], st[nt][h8 + 1]);
+#pragma unroll
+        for (int v = 2; v < 8; v += 2) mx = fmaxf(mx, fmaxf(st[nt][h8 + v], st[nt][h8 + v + 1]));
+        part[nt][(m - 8) & 1] = mx;
+    } else if (m == 12 || m == 14) {
+        const int nt = (m - 12) >> 1;
+        part[nt][0] = max_across_halves(fmaxf(part[nt][0], part[nt][1]));
+    } else {
+        const int nt = (m - 13) >> 1;
+        const float mx = part[nt][0];
+        if (fs.mref[nt] == -__builtin_inff()) fs.mref[nt] = mx;
+        fs.growth[nt] = fmaxf(fs.growth[nt], mx - fs.mref[nt]);
+        msub[nt] = fs.mref[nt] == -__builtin_inff() ? 0.f : fs.mref[nt];
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void pv_then_head(const bf16x8 (&vA)[D / 32][2], const bf16x8 (&pB)[2][2],
+                                             FixedState<D>& fs, f32x16 (&st)[2], const TileRef& cur,
+                                             int u, const float* srow, int half, float scale2,
+                                             float (&msub)[2]) {
+    constexpr int NM = 4 * (D / 32);  // PV MFMAs of a half
+    const float* b = srow + cur.bias_off + 32 * u + 4 * half;
+    f32x4 bb[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) bb[g] = *reinterpret_cast<const f32x4*>(b + 8 * g);
+    float part[2][2];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) mfma_pv_acc(fs.oacc[mt][nt], vA[mt][s], pB[nt][s]);
+            for (int nt = 0; nt < 2; ++nt) {
+                const int k = (s * (D / 32) + mt) * 2 + nt;
+                mfma_pv_acc(fs.oacc[mt][nt], vA[mt][s], pB[nt][s]);
+#pragma unroll
+                for (int m = k * 16 / NM; m < (k + 1) * 16 / NM; ++m)
+                    head_slice<D>(m, st, bb, scale2, fs, msub, part);
+                __builtin_amdgcn_sched_barrier(0);
+            }
 }
 
 // O = acc / l rounded to bf16; lane holds query 32*nt + l32 and
@@ -486,7 +534,8 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     // loads that the in-order vmcnt waits rely on, in place):
     //   S^T of half h+1 beside the exp2 work of half h;
     //   loads of the values of half h+1, then of the keys of half h+3;
-    //   PV of half h beside the logits, maxima and bias of half h+1.
+    //   PV of half h with the logits, maxima and bias of half h+1 placed
+    //   between its MFMAs by hand (pv_then_head).
     // Past the end the prefetches and the S^T products re-read the last tile
     // (their results are never used), so every iteration runs the same
     // straight-line code; a repeated half cannot raise a row's maximum.
@@ -536,9 +585,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             load_k<D>(t1, 1, lane, kB1);
             __builtin_amdgcn_sched_barrier(0);
-            pv_product_acc<D>(vB0, pB, fs);                  // PV (t, 0)
-            softmax_head_fixed<D>(st1, t0, 1, srow, half, scale2, fs, msub1);
-            interleave<16, 4>();
+            pv_then_head<D>(vB0, pB, fs, st1, t0, 1, srow, half, scale2, msub1);  // PV (t, 0)
             __builtin_amdgcn_sched_barrier(0);
             s_product<D>(kB0, qB, st0);                      // S^T (t+1, 0)
             softmax_tail(st1, msub1, fs, pB);                // exp2 (t, 1)
@@ -548,9 +595,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             load_k<D>(t2, 0, lane, kB0);
             __builtin_amdgcn_sched_barrier(0);
-            pv_product_acc<D>(vB1, pB, fs);                  // PV (t, 1)
-            softmax_head_fixed<D>(st0, t1, 0, srow, half, scale2, fs, msub0);
-            interleave<16, 4>();
+            pv_then_head<D>(vB1, pB, fs, st0, t1, 0, srow, half, scale2, msub0);  // PV (t, 1)
             __builtin_amdgcn_sched_barrier(0);
             t0 = t1;
             t1 = t2;
