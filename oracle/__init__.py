@@ -20,7 +20,7 @@ _SRC = os.path.join(_HERE, "solattn_oracle.c")
 _LIB = os.path.join(_HERE, "libsolattn_oracle.so")
 _lib = None
 
-DENSE, SPARSE = 0, 1
+DENSE, SPARSE, TOPK = 0, 1, 2
 BLOCK = 64
 
 

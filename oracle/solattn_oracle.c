@@ -41,6 +41,17 @@
  *
  * DENSE mode keeps every block (plain softmax attention).  A mask override
  * replaces the routing decision with the caller's keep bits.
+ *
+ * TOPK mode is the draft stage's fixed-ratio block-sparse attention (page
+ * "英伟达开源 Sol-H3，给 MiniMax-H3 加速，5 秒视频 1.4 秒出", section 2.1: the
+ * draft keeps a fixed 90 % video sparsity with 64-token blocks on a
+ * block-sparse attention backend).  tau is then the kept fraction f of the
+ * video (non-prefix) key blocks: with Nv = Nb - Pb and k = ceil(f * Nv),
+ * query block i keeps the prefix and every video block whose score is at
+ * least the k-th largest video score of its row (ties at that score are all
+ * kept).  The pages do not say how the draft picks its blocks; ranking by the
+ * same pooled score is the reading taken.  Skipped blocks contribute nothing
+ * (plain block-sparse attention, no pooled term).
  */
 #include <math.h>
 #include <stdint.h>
@@ -52,7 +63,7 @@
 
 #define ORACLE_BLOCK 64
 
-enum { ORACLE_DENSE = 0, ORACLE_SPARSE = 1 };
+enum { ORACLE_DENSE = 0, ORACLE_SPARSE = 1, ORACLE_TOPK = 2 };
 
 /* Number of tokens in block j. */
 static int64_t block_len(int64_t N, int64_t j) {
@@ -94,9 +105,33 @@ static double row_threshold(const double* s, int64_t Nb, double tau) {
     return mu + tau * sigma;
 }
 
-/* Step 5 for one query row. */
+static int cmp_desc(const void* a, const void* b) {
+    double x = *(const double*)a, y = *(const double*)b;
+    return (x < y) - (x > y);
+}
+
+/* TOPK mode: the k-th largest of the video scores s[Pb..Nb) (k >= 1), found
+ * by sorting a copy; +inf when k = 0 (nothing but the prefix is kept). */
+static double kth_largest(const double* s, int64_t Pb, int64_t Nb, int64_t k, double* scratch) {
+    if (k < 1) return INFINITY;
+    int64_t nv = Nb - Pb;
+    memcpy(scratch, s + Pb, sizeof(double) * nv);
+    qsort(scratch, (size_t)nv, sizeof(double), cmp_desc);
+    return scratch[k - 1];
+}
+
+/* Number of video key blocks TOPK mode keeps per row: ceil(f * (Nb - Pb)),
+ * evaluated in double. */
+static int64_t topk_count(double f, int64_t Pb, int64_t Nb) {
+    int64_t nv = Nb - Pb;
+    int64_t k = (int64_t)ceil(f * (double)nv);
+    return k > nv ? nv : k;
+}
+
+/* Step 5 for one query row.  `pooled` = skipped blocks add their pooled term
+ * (Sol-Attn); 0 = they contribute nothing (TOPK's block-sparse attention). */
 static void attend_row(const double* qr, const double* k, const double* v,
-                       const double* kbar, const double* vbar, const uint8_t* keep,
+                       const double* kbar, const double* vbar, const uint8_t* keep, int pooled,
                        int64_t N, int64_t d, double* logit_buf, double* o) {
     int64_t Nb = (N + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
     double scale = 1.0 / sqrt((double)d);
@@ -110,7 +145,7 @@ static void attend_row(const double* qr, const double* k, const double* v,
                 logit_buf[n_terms++] = e;
                 if (e > m) m = e;
             }
-        } else {
+        } else if (pooled) {
             double e = dot(qr, kbar + j * d, d) * scale;
             logit_buf[n_terms++] = e;
             if (e > m) m = e;
@@ -127,7 +162,7 @@ static void attend_row(const double* qr, const double* k, const double* v,
                 den += w;
                 for (int64_t c = 0; c < d; ++c) o[c] += w * v[t * d + c];
             }
-        } else {
+        } else if (pooled) {
             double w = (double)block_len(N, j) * exp(logit_buf[n_terms++] - m);
             den += w;
             for (int64_t c = 0; c < d; ++c) o[c] += w * vbar[j * d + c];
@@ -139,7 +174,8 @@ static void attend_row(const double* qr, const double* k, const double* v,
 /*
  * One (b, h) slice.
  *   q, k, v      [N][d] fp64.
- *   mode         0 dense, 1 sparse.
+ *   mode         0 dense, 1 sparse (Sol-Attn), 2 topk (tau = kept fraction of
+ *                the video key blocks, 0 < tau <= 1; no pooled terms).
  *   mask_override [Nb][Nb] keep bits (0/1) or NULL; when given it is used
  *                as is (no prefix forcing) in either mode.
  *   qblocks      list of query blocks to produce, or NULL for all of them.
@@ -148,7 +184,8 @@ static void attend_row(const double* qr, const double* k, const double* v,
  *                or NULL: rows of the listed query blocks are written.
  *   qbar_out, kbar_out, vbar_out  [Nb][d] or NULL (all blocks).
  * Returns 0, or -1 for invalid arguments (d < 1, N < 1, prefix_len outside
- * [0, N], NaN tau, unknown mode), or -2 when memory runs out.
+ * [0, N], NaN tau, unknown mode, topk fraction outside (0, 1]), or -2 when
+ * memory runs out.
  */
 int solattn_oracle_head(const double* q, const double* k, const double* v,
                         int64_t N, int64_t d, int64_t prefix_len, double tau, int mode,
@@ -157,8 +194,9 @@ int solattn_oracle_head(const double* q, const double* k, const double* v,
                         double* score_out, double* thr_out, double* qbar_out,
                         double* kbar_out, double* vbar_out, int threads) {
     if (!q || !k || !v || N < 1 || d < 1 || prefix_len < 0 || prefix_len > N || isnan(tau) ||
-        (mode != ORACLE_DENSE && mode != ORACLE_SPARSE))
+        (mode != ORACLE_DENSE && mode != ORACLE_SPARSE && mode != ORACLE_TOPK))
         return -1;
+    if (mode == ORACLE_TOPK && !(tau > 0.0 && tau <= 1.0)) return -1;
     int64_t Nb = (N + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
     int64_t Pb = (prefix_len + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
     double* qbar = (double*)malloc(sizeof(double) * Nb * d);
@@ -188,8 +226,9 @@ int solattn_oracle_head(const double* q, const double* k, const double* v,
         uint8_t* keep = (uint8_t*)malloc(Nb);
         double* s = (double*)malloc(sizeof(double) * Nb);
         double* logit_buf = (double*)malloc(sizeof(double) * (N + Nb));
-        if (!keep || !s || !logit_buf) {
-            free(keep); free(s); free(logit_buf);
+        double* sorted = (double*)malloc(sizeof(double) * Nb);
+        if (!keep || !s || !logit_buf || !sorted) {
+            free(keep); free(s); free(logit_buf); free(sorted);
             err = -2;
             continue;
         }
@@ -201,6 +240,9 @@ int solattn_oracle_head(const double* q, const double* k, const double* v,
             for (int64_t j = 0; j < Nb; ++j) keep[j] = mask_override[i * Nb + j] ? 1 : 0;
         } else if (mode == ORACLE_DENSE) {
             for (int64_t j = 0; j < Nb; ++j) keep[j] = 1;
+        } else if (mode == ORACLE_TOPK) {
+            thr = kth_largest(s, Pb, Nb, topk_count(tau, Pb, Nb), sorted);
+            for (int64_t j = 0; j < Nb; ++j) keep[j] = (j < Pb) || (s[j] >= thr);
         } else {
             thr = row_threshold(s, Nb, tau);
             for (int64_t j = 0; j < Nb; ++j) keep[j] = (j < Pb) || (s[j] >= thr);
@@ -211,9 +253,10 @@ int solattn_oracle_head(const double* q, const double* k, const double* v,
         /* step 5: output rows of this query block */
         if (out) {
             for (int64_t r = i * ORACLE_BLOCK; r < i * ORACLE_BLOCK + block_len(N, i); ++r)
-                attend_row(q + r * d, k, v, kbar, vbar, keep, N, d, logit_buf, out + r * d);
+                attend_row(q + r * d, k, v, kbar, vbar, keep, mode != ORACLE_TOPK, N, d,
+                           logit_buf, out + r * d);
         }
-        free(keep); free(s); free(logit_buf);
+        free(keep); free(s); free(logit_buf); free(sorted);
     }
     free(qbar); free(kbar); free(vbar);
     return err;

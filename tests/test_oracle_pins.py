@@ -330,3 +330,87 @@ def test_tiny_workload_end_to_end():
     assert np.isfinite(r["out"]).all()
     m = r["mask"][0, 0]
     assert m[:, :2].all() and 0 < m.mean() < 1
+
+
+# ------------------------------------------------- fixed-ratio (TOPK) routing
+def brute_block_sparse(q, k, v, keep_row, nb):
+    """softmax over the keys of the kept blocks only, written independently."""
+    cols = np.concatenate([np.arange(64 * j, min(64 * j + 64, k.shape[0]))
+                           for j in range(nb) if keep_row[j]])
+    return brute_dense(q, k[cols], v[cols])
+
+
+def test_topk_worked_examples():
+    # prefix block 0, video scores [1, 4, 1, 5, 9, 2, 6]:
+    #   f = 0.3 -> k = ceil(2.1) = 3 -> top three {9, 6, 5} -> threshold 5
+    #   f = 1/7 -> k = ceil(1.0) = 1 -> {9}, threshold 9 (exact multiple)
+    #   f = 0.5 -> k = ceil(3.5) = 4 -> {9, 6, 5, 4}, threshold 4
+    #   f = 1   -> every block
+    scores = [3.0, 1.0, 4.0, 1.0, 5.0, 9.0, 2.0, 6.0]
+    q, k, v = _score_row_inputs(scores)
+    for f, thr, keep in ((0.3, 5.0, [1, 0, 0, 0, 1, 1, 0, 1]),
+                         (1.0 / 7.0, 9.0, [1, 0, 0, 0, 0, 1, 0, 0]),
+                         (0.5, 4.0, [1, 0, 1, 0, 1, 1, 0, 1]),
+                         (1.0, 1.0, [1] * 8)):
+        r = oracle.head(q, k, v, 64, f, mode=oracle.TOPK, want_out=False)
+        assert r["thr"][0] == thr, f
+        assert list(r["mask"][0]) == keep, f
+
+
+def test_topk_ties_at_the_threshold_are_all_kept():
+    # video scores [2, 7, 7, 3], f = 0.25 -> k = 1 -> threshold 7, both 7s kept
+    q, k, v = _score_row_inputs([0.0, 2.0, 7.0, 7.0, 3.0])
+    r = oracle.head(q, k, v, 64, 0.25, mode=oracle.TOPK, want_out=False)
+    assert list(r["mask"][0]) == [1, 0, 1, 1, 0]
+
+
+def test_topk_no_video_blocks_keeps_the_prefix():
+    q, k, v = rand_head(300, 16, 40)
+    r = oracle.head(q, k, v, 300, 0.1, mode=oracle.TOPK)
+    assert r["mask"].all()
+    assert np.allclose(r["out"], brute_dense(q, k, v), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("N,prefix,f", [(1000, 128, 0.1), (777, 0, 0.25), (640, 64, 0.5)])
+def test_topk_counts_and_ranking(N, prefix, f):
+    q, k, v = rand_head(N, 32, 41)
+    nb = (N + 63) // 64
+    pb = (prefix + 63) // 64
+    kk = min(nb - pb, math.ceil(f * (nb - pb)))
+    r = oracle.head(q, k, v, prefix, f, mode=oracle.TOPK, want_out=False)
+    for i in range(nb):
+        s = r["score"][i]
+        vid = np.arange(pb, nb)
+        top = set(vid[np.argsort(-s[pb:], kind="stable")][:kk].tolist())
+        kept = set(np.nonzero(r["mask"][i][pb:])[0] + pb)
+        assert kept == top                                    # distinct scores: exactly the top k
+        assert r["mask"][i][:pb].all()
+        assert r["thr"][i] == np.sort(s[pb:])[::-1][kk - 1]
+
+
+@pytest.mark.parametrize("N,prefix,f", [(700, 64, 0.2), (333, 0, 0.5)])
+def test_topk_output_is_block_sparse_softmax(N, prefix, f):
+    # skipped blocks contribute nothing: each row is a softmax over the kept
+    # blocks' keys alone
+    q, k, v = rand_head(N, 16, 42)
+    nb = (N + 63) // 64
+    r = oracle.head(q, k, v, prefix, f, mode=oracle.TOPK)
+    for i in range(nb):
+        rows = slice(64 * i, min(64 * i + 64, N))
+        ref = brute_block_sparse(q[rows], k, v, r["mask"][i], nb)
+        assert np.allclose(r["out"][rows], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_topk_fraction_one_is_dense():
+    q, k, v = rand_head(500, 16, 43)
+    a = oracle.head(q, k, v, 64, 1.0, mode=oracle.TOPK)
+    b = oracle.head(q, k, v, 64, 0.0, mode=oracle.DENSE)
+    assert a["mask"].all()
+    assert np.array_equal(a["out"], b["out"])
+
+
+def test_topk_rejects_fraction_outside_unit_interval():
+    q, k, v = rand_head(128, 8, 44)
+    for f in (0.0, -0.5, 1.5, float("inf"), float("nan")):
+        with pytest.raises(ValueError):
+            oracle.head(q, k, v, 0, f, mode=oracle.TOPK)
