@@ -43,9 +43,9 @@
  * replaces the routing decision with the caller's keep bits.
  *
  * TOPK mode is the draft stage's fixed-ratio block-sparse attention (page
- * "英伟达开源 Sol-H3，给 MiniMax-H3 加速，5 秒视频 1.4 秒出", section 2.1: the
- * draft keeps a fixed 90 % video sparsity with 64-token blocks on a
- * block-sparse attention backend).  tau is then the kept fraction f of the
+ * "NVIDIA 团队开源 Sol-H3 的 DGX Spark 版本", section "潜空间直传：384p 草稿到
+ * 768p 精修": the draft runs its attention at a fixed 90 % video sparsity
+ * with 64-token blocks on a block-sparse attention backend).  tau is then the kept fraction f of the
  * video (non-prefix) key blocks: with Nv = Nb - Pb and k = ceil(f * Nv),
  * query block i keeps the prefix and every video block whose score is at
  * least the k-th largest video score of its row (ties at that score are all
