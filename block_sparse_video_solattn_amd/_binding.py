@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsolattn.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
-DENSE, SPARSE = 0, 1
+DENSE, SPARSE, TOPK = 0, 1, 2
 F32, BF16 = 0, 1
 
 if not os.path.exists(LIB_PATH):
@@ -104,7 +104,7 @@ def _dtype_code(t) -> int:
 
 def _mode_code(mode) -> int:
     if isinstance(mode, str):
-        return {"dense": DENSE, "sparse": SPARSE}[mode]
+        return {"dense": DENSE, "sparse": SPARSE, "topk": TOPK}[mode]
     return int(mode)
 
 

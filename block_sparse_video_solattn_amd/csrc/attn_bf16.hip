@@ -467,7 +467,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
 
     int n_kept;
     uint64_t tile_mask;
-    if (a.mode == kSparse) {
+    if (a.mode != kDense) {
         const RouteResult r = route_query_block<D>(a, bh, i, srow, klist);
         n_kept = r.n_kept;
         tile_mask = r.tile_mask;
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     auto tile_at = [&](int t) -> TileRef {
         TileRef r;
         if (t < n_kept) {
-            const int64_t j = (a.mode == kSparse)
+            const int64_t j = (a.mode != kDense)
                                   ? (int64_t)__builtin_amdgcn_readfirstlane((int)klist[t])
                                   : (int64_t)t;
             r.ktile = kp + j * (int64_t)D * 64;
@@ -609,7 +609,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     }
     if (!abandoned) return;
 
-    attend_rescaling<D>(qp, kp, vp, kbp, vbp, op, N, Nb, Nbp, a.mode == kSparse, i, n_kept, tile_mask,
+    attend_rescaling<D>(qp, kp, vp, kbp, vbp, op, N, Nb, Nbp, a.mode != kDense, i, n_kept, tile_mask,
                         srow, klist, plist);
 }
 

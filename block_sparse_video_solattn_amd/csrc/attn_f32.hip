@@ -30,7 +30,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
     int n_kept;
     uint64_t tile_mask;
-    if (a.mode == kSparse) {
+    if (a.mode != kDense) {
         const RouteResult r = route_query_block<D>(a, bh, i, srow, klist);
         n_kept = r.n_kept;
         tile_mask = r.tile_mask;
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
         const float* vsrc;
         int nrows, ptile = -1;
         if (t < n_kept) {
-            const int64_t j = (a.mode == kSparse) ? (int64_t)klist[t] : (int64_t)t;
+            const int64_t j = (a.mode != kDense) ? (int64_t)klist[t] : (int64_t)t;
             ksrc = kp + j * 64 * D;
             vsrc = vp + j * 64 * D;
             nrows = (int)((j + 1) * 64 <= N ? 64 : N - j * 64);

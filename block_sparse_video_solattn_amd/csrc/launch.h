@@ -9,7 +9,7 @@
 namespace solattn {
 
 enum Dtype { kF32 = 0, kBF16 = 1 };
-enum Mode { kDense = 0, kSparse = 1 };
+enum Mode { kDense = 0, kSparse = 1, kTopk = 2 };
 
 // Workspace regions (byte offsets, each 256-byte aligned).  BH = B*H,
 // Nb = ceil(N/64), Nbp = Nb rounded up to a multiple of 64.
@@ -61,7 +61,7 @@ struct PoolArgs {
     void* vP;
     int64_t N, Nb, Nbp;
     int d, dtype;
-    int pooled;   // compute block means (sparse mode)
+    int pooled;   // compute block means (sparse and topk modes)
     int pack;     // write the operand-ordered key and value tiles (bf16)
 };
 
@@ -84,6 +84,7 @@ struct AttnArgs {
     int64_t BH, N, Nb, Nbp;
     int64_t Pb;
     float tau;
+    int64_t topk;         // kTopk: video key blocks kept per query block
     int d, dtype, mode;
 };
 

@@ -12,6 +12,9 @@
 // over all Nb key blocks; a score equal to the threshold is kept; tau = -inf
 // keeps all, tau = +inf keeps only the prefix, sigma = 0 uses the mean.
 //
+// In the fixed-ratio mode the threshold is instead the k-th largest video
+// score of the row (kth_largest_video) and skipped blocks get no pooled term.
+//
 // Nothing of the routing reaches device memory except through the debug
 // exports: the mask lives as ballot words, the kept-block list and the
 // pooled-term biases in LDS.
@@ -21,6 +24,36 @@
 #include "launch.h"
 
 namespace solattn {
+
+// Fixed-ratio routing (the draft stage's block-sparse attention at a fixed
+// video sparsity, page "NVIDIA 团队开源 Sol-H3 的 DGX Spark 版本", section
+// "潜空间直传：384p 草稿到 768p 精修"): the k-th largest of the video scores
+// s[Pb..Nb) of a row, k >= 1, exactly, or +inf for k = 0.  Scores are mapped
+// to order-preserving unsigned keys and the key of the k-th largest is built
+// bit by bit from the top: a bit stays set when at least k keys are >= the
+// candidate.  One wavefront; the row is in LDS.
+__device__ inline uint32_t order_key(float x) {
+    const uint32_t b = __float_as_uint(x);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ inline float kth_largest_video(const float* srow, int64_t Pb, int64_t Nb, int64_t k) {
+    if (k < 1) return __builtin_inff();
+    const int lane = threadIdx.x & 63;
+    uint32_t key = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = key | (1u << bit);
+        int64_t count = 0;
+        for (int64_t j0 = 0; j0 < Nb; j0 += 64) {
+            const int64_t j = j0 + lane;
+            const bool ge = j >= Pb && j < Nb && order_key(srow[j]) >= cand;
+            count += __popcll(__ballot(ge));
+        }
+        if (count >= k) key = cand;
+    }
+    const uint32_t b = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
+    return __uint_as_float(b);
+}
 
 struct RouteResult {
     int n_kept;          // kept key blocks, listed ascending in klist[0..n_kept)
@@ -61,23 +94,27 @@ __device__ inline RouteResult route_query_block(const AttnArgs& a, int64_t bh, i
     }
     __syncthreads();
 
-    // row statistics, two passes (mean, then squared deviations)
-    float part = 0.f;
-    for (int64_t j = lane; j < Nb; j += 64) part += srow[j];
-    const float mu = wave_sum(part) / (float)Nb;
-    part = 0.f;
-    for (int64_t j = lane; j < Nb; j += 64) {
-        const float t = srow[j] - mu;
-        part += t * t;
-    }
-    const float sigma = sqrtf(wave_sum(part) / (float)Nb);
     float thr;
-    if (__builtin_isinf(a.tau))
-        thr = a.tau;
-    else if (sigma == 0.f)
-        thr = mu;
-    else
-        thr = mu + a.tau * sigma;
+    if (a.mode == kTopk) {
+        thr = kth_largest_video(srow, a.Pb, Nb, a.topk);
+    } else {
+        // row statistics, two passes (mean, then squared deviations)
+        float part = 0.f;
+        for (int64_t j = lane; j < Nb; j += 64) part += srow[j];
+        const float mu = wave_sum(part) / (float)Nb;
+        part = 0.f;
+        for (int64_t j = lane; j < Nb; j += 64) {
+            const float t = srow[j] - mu;
+            part += t * t;
+        }
+        const float sigma = sqrtf(wave_sum(part) / (float)Nb);
+        if (__builtin_isinf(a.tau))
+            thr = a.tau;
+        else if (sigma == 0.f)
+            thr = mu;
+        else
+            thr = mu + a.tau * sigma;
+    }
 
     // keep bits, kept list, pooled-tile flags, pooled biases
     int n_kept = 0;
@@ -100,7 +137,7 @@ __device__ inline RouteResult route_query_block(const AttnArgs& a, int64_t bh, i
         }
         if (keep) klist[n_kept + __popcll(kb & lt)] = (uint16_t)j;
         n_kept += __popcll(kb);
-        if (sb) tile_mask |= 1ull << (j0 / 64);
+        if (sb && a.mode == kSparse) tile_mask |= 1ull << (j0 / 64);  // pooled terms: Sol-Attn only
         const int nj = (int)((j + 1) * 64 <= a.N ? 64 : a.N - j * 64);
         srow[j] = skip ? log2f((float)nj) : -__builtin_inff();
     }

@@ -57,8 +57,11 @@ int validate(const void* q, const void* k, const void* v, const void* out, bool 
     if (prefix_len < 0 || prefix_len > N)
         return fail(SOLATTN_EINVAL, "prefix_len must lie in [0, N] (got %lld)", (long long)prefix_len);
     if (std::isnan(tau)) return fail(SOLATTN_EINVAL, "tau must not be NaN");
-    if (mode != SOLATTN_DENSE && mode != SOLATTN_SPARSE)
+    if (mode != SOLATTN_DENSE && mode != SOLATTN_SPARSE && mode != SOLATTN_TOPK)
         return fail(SOLATTN_EINVAL, "unknown mode %d", mode);
+    if (mode == SOLATTN_TOPK && need_out && !(tau > 0.f && tau <= 1.f))
+        return fail(SOLATTN_EINVAL, "topk mode: tau is the kept fraction, in (0, 1] (got %g)",
+                    (double)tau);
     if (dtype != SOLATTN_F32 && dtype != SOLATTN_BF16)
         return fail(SOLATTN_EINVAL, "unknown dtype %d", dtype);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (out && !aligned16(out)))
@@ -137,7 +140,7 @@ int run_prepare(const void* q, const void* k, const void* v, int64_t B, int64_t 
     p.Nbp = (p.Nb + 63) / 64 * 64;
     p.d = (int)d;
     p.dtype = dtype;
-    p.pooled = mode == SOLATTN_SPARSE;
+    p.pooled = mode != SOLATTN_DENSE;
     p.pack = pack && dtype == kBF16;
     if (!p.pooled && !p.pack) return SOLATTN_OK;  // fp32 dense: nothing to prepare
     hipError_t e = launch_pool(p, B * H, s);
@@ -164,7 +167,7 @@ int run_attend(const void* q, const void* k, const void* v, void* out, int64_t B
     a.kbarT = reinterpret_cast<const float*>(at(ws, L.kbarT));
     a.out = out;
     a.mask_out = mask_out;
-    a.score_out = mode == SOLATTN_SPARSE ? score_out : nullptr;
+    a.score_out = mode != SOLATTN_DENSE ? score_out : nullptr;
     a.thr_out = thr_out;
     a.BH = B * H;
     a.N = N;
@@ -175,6 +178,13 @@ int run_attend(const void* q, const void* k, const void* v, void* out, int64_t B
     a.d = (int)d;
     a.dtype = dtype;
     a.mode = mode;
+    // topk: k = ceil(tau * video key blocks), evaluated in double on the host
+    // so that every query block (and any reference) uses the same count
+    {
+        const int64_t nv = a.Nb - a.Pb;
+        int64_t kk = mode == SOLATTN_TOPK ? (int64_t)std::ceil((double)tau * (double)nv) : 0;
+        a.topk = kk > nv ? nv : kk;
+    }
     hipError_t e = route_only ? launch_route(a, s)
                               : dtype == kBF16 ? launch_attn_bf16(a, s) : launch_attn_f32(a, s);
     if (e != hipSuccess) return hip_fail(e, route_only ? "route kernel launch" : "attention kernel launch");

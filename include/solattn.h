@@ -64,6 +64,18 @@ extern "C" {
 /* mode */
 #define SOLATTN_DENSE 0  /* every key block exact (plain softmax attention) */
 #define SOLATTN_SPARSE 1 /* Sol-Attn routing */
+/*
+ * Fixed-ratio block-sparse attention, the draft stage's scheme (page "NVIDIA
+ * 团队开源 Sol-H3 的 DGX Spark 版本", section "潜空间直传：384p 草稿到 768p
+ * 精修": a fixed 90 % video sparsity with 64-token blocks on a block-sparse
+ * attention backend).  tau is then the kept fraction f of the video
+ * (non-prefix) key blocks, 0 < f <= 1: with Nv = Nb - ceil(prefix_len/64)
+ * and k = ceil(f * Nv) (evaluated in double from the float f), query block i
+ * keeps the prefix blocks and every video block whose score s_ij (as above)
+ * is at least the k-th largest video score of row i (ties all kept).  Skipped
+ * blocks contribute nothing: no pooled term.
+ */
+#define SOLATTN_TOPK 2
 
 /* dtype */
 #define SOLATTN_F32 0
@@ -72,7 +84,8 @@ extern "C" {
 /*
  * Full forward pass: pooling (step 1) then the fused routing + attention
  * kernel (steps 2-5).  In DENSE mode tau and prefix_len are ignored and no
- * pooling is done.  Uses an internal per-device workspace that grows on
+ * pooling is done; in TOPK mode tau is the kept fraction (outside (0, 1]:
+ * SOLATTN_EINVAL).  Uses an internal per-device workspace that grows on
  * demand (the growth synchronises the device once).
  */
 int solattn_forward(const void* q, const void* k, const void* v, void* out, int64_t B,
@@ -111,8 +124,9 @@ int solattn_attend_ws(const void* q, const void* k, const void* v, void* out, in
  * the same device code: mask_out [B][H][Nb][ceil(Nb/32)] uint32 words (bit
  * j%32 of word j/32 in row i is keep_ij), score_out [B][H][Nb][Nb] fp32
  * scores s_ij, thr_out [B][H][Nb] fp32 thresholds (-inf / +inf for tau =
- * -inf / +inf; -inf in DENSE mode, where the mask is all ones).  Any export
- * pointer may be NULL.  For tests and measurement only.
+ * -inf / +inf; -inf in DENSE mode, where the mask is all ones; in TOPK mode
+ * the k-th largest video score, +inf when k = 0).  Any export pointer may be
+ * NULL.  For tests and measurement only.
  */
 int solattn_forward_debug(const void* q, const void* k, const void* v, void* out, int64_t B,
                           int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau,

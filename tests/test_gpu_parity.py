@@ -26,26 +26,29 @@ def check_forward(q, k, v, dtype, prefix, tau, mode="sparse", rows_blocks=None):
     """GPU forward vs oracle recomputed with the GPU's mask; returns stats."""
     B, H, N, d = q.shape
     gout, gmask, gs, gthr = gpu_debug(q, k, v, dtype, prefix, tau, mode)
+    omode = {"sparse": oracle.SPARSE, "dense": oracle.DENSE, "topk": oracle.TOPK}[mode]
+    otau = float(np.float32(tau))  # the value the C ABI received
     n_diff = n_near = 0
     worst = 0.0
     for b in range(B):
         for h in range(H):
-            ores = oracle.head(q[b, h], k[b, h], v[b, h], prefix, tau,
-                               mode=oracle.SPARSE if mode == "sparse" else oracle.DENSE,
+            ores = oracle.head(q[b, h], k[b, h], v[b, h], prefix, otau, mode=omode,
                                want_out=False)
-            if mode == "sparse":
+            if mode != "dense":
                 nd, nn = mask_compare(gmask, ores, b, h)
                 n_diff += nd
                 n_near += nn
                 fin = np.isfinite(ores["score"])
                 assert np.max(np.abs(gs[b, h][fin] - ores["score"][fin])) < 1e-4
-                if not math.isinf(tau):
-                    assert np.max(np.abs(gthr[b, h] - ores["thr"])) < 1e-4
-                else:
+                if mode == "sparse" and math.isinf(tau):
                     assert np.all(gthr[b, h] == tau)
+                else:
+                    fin_t = np.isfinite(ores["thr"])
+                    assert np.array_equal(np.isfinite(gthr[b, h]), fin_t)
+                    assert np.max(np.abs(gthr[b, h][fin_t] - ores["thr"][fin_t]), initial=0) < 1e-4
             else:
                 assert gmask[b, h].all()
-            r = oracle.head(q[b, h], k[b, h], v[b, h], prefix, tau,
+            r = oracle.head(q[b, h], k[b, h], v[b, h], prefix, otau, mode=omode,
                             mask_override=gmask[b, h].astype(np.uint8), qblocks=rows_blocks)
             rows = None if rows_blocks is None else block_rows(rows_blocks, N)
             ab, rel = out_error(gout[b, h], r["out"], rows)
@@ -208,6 +211,39 @@ def test_steep_logit_rise_after_first_block(mode, scale):
 def test_steep_logit_rise_f32():
     q, k, v = inputs.logit_jump(1, 1, 64 * 9 + 7, 64, "f32", jump_block=3, scale=10.0, seed=42)
     check_forward(q, k, v, "f32", 64, 1.0)
+
+
+# ------------------------------------------------- fixed-ratio (TOPK) mode
+@pytest.mark.parametrize("dtype,N,d,prefix,f", [
+    ("bf16", 2000, 128, 128, 0.1), ("bf16", 64 * 9 + 20, 64, 0, 0.25), ("f32", 1024, 64, 128, 0.3),
+    ("bf16", 700, 128, 64, 1.0), ("bf16", 1500, 128, 1500, 0.1)])
+def test_topk_mode(dtype, N, d, prefix, f):
+    q, k, v = inputs.custom(1, 2, N, d, dtype, prefix_len=prefix, seed=51)
+    st = check_forward(q, k, v, dtype, prefix, f, "topk")
+    nb = (N + 63) // 64
+    pb = (prefix + 63) // 64
+    kk = min(nb - pb, math.ceil(float(np.float32(f)) * (nb - pb)))
+    # every row keeps its prefix and (distinct scores) exactly k video blocks
+    assert st["mask"][..., :pb].all()
+    assert (st["mask"][..., pb:].sum(-1) == kk).all()
+
+
+def test_topk_draft_fraction_field_inputs():
+    # the draft stage's 90 % video sparsity on field inputs (ragged tail)
+    q, k, v = inputs.custom(1, 2, 4000, 128, "bf16", prefix_len=256, seed=52, kind="field",
+                            grid=(4, 24, 40))
+    check_forward(q, k, v, "bf16", 256, 0.1, "topk")
+
+
+def test_topk_fraction_one_matches_dense():
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    q, k, v = inputs.custom(1, 2, 1800, 128, "bf16", seed=53)
+    qd, kd, vd = device_tensors(q, k, v, "bf16")
+    a = sa.solattn_forward(qd, kd, vd, None, 64, 1.0, "topk")
+    b = sa.solattn_forward(qd, kd, vd, None, 64, 0.0, "dense")
+    torch.cuda.synchronize()
+    assert (a.float() - b.float()).abs().max().item() <= 1e-2
 
 
 def test_pooled_only_path_f32():
