@@ -129,15 +129,24 @@ def draft_check(sa, stream):
 
     def dense():
         sa.solattn_forward_ws(qd, kd, vd, out, w.prefix_len, 0.0, "dense", ws)
+    # the draft stage's own scheme: fixed 10 % of the video key blocks kept,
+    # no pooled term (block-sparse attention)
+    def topk():
+        sa.solattn_forward_ws(qd, kd, vd, out, w.prefix_len, 0.1, "topk", ws)
     for _ in range(3):
         sparse()
     sms = float(np.median(time_calls(sparse, 20, stream)))
+    for _ in range(3):
+        topk()
+    tms = float(np.median(time_calls(topk, 20, stream)))
     dense()
     dms = float(np.median(time_calls(dense, 5, stream)))
     return {"workload": "draft: 672x384 -> 32x24x42 latent, 512 prefix + 32256 video tokens",
             "N": w.N, "tau": tau, "video_sparsity": round(float(1 - m[..., pb:].mean()), 4),
             "sparse_ms": round(sms, 4), "dense_ms": round(dms, 3),
-            "speedup_vs_dense": round(dms / sms, 2)}
+            "speedup_vs_dense": round(dms / sms, 2),
+            "fixed_ratio_10pct": {"mode": "topk", "keep_fraction": 0.1, "ms": round(tms, 4),
+                                  "speedup_vs_dense": round(dms / tms, 2)}}
 
 
 def main():
