@@ -29,12 +29,15 @@
 //     with logit c q.kbar_j + ln n_j, so it shares the MFMA body and the
 //     online-softmax state with the exact tiles;
 //   * the online softmax runs in log2 units (exp2).  The fast path fixes
-//     each row's reference at the maximum of its first half with a finite
-//     logit and never rescales: weights up to 2^64 above it stay far from
-//     the fp32/bf16 range limit.  If some row's maximum rose further, the
-//     fast path's result is discarded after its loop and the query block is
-//     recomputed from the start by the rescaling path (VGPR accumulators,
-//     lazy rescale when the maximum grows by more than 2^8).  The denominator adds the
+//     each row's reference mref at the maximum of the first half and never
+//     rescales: weights up to 2^64 above it stay far from the fp32/bf16
+//     range limit.  Every later S^T accumulation starts from -mref/scale2
+//     instead of zero, so its logits come out relative to the reference and
+//     the exp2 needs no subtraction.  If some row's first half has no
+//     finite logit, or some row's maximum later rose more than 2^64 above
+//     the reference, the fast path's result is discarded and the query
+//     block is recomputed from the start by the rescaling path (VGPR
+//     accumulators, lazy rescale when the maximum grows by more than 2^8).  The denominator adds the
 //     bf16-rounded weights the MFMA consumes (v_dot2 against (1, 1)), so
 //     numerator and denominator agree;
 //   * workgroups are remapped so that the query blocks of one head run on
@@ -144,6 +147,23 @@ __device__ __forceinline__ void s_product(const bf16x8 (&kA)[D / 16],
     }
 }
 
+// S^T for one half with the accumulation started from `c` instead of zero:
+// the fast path starts from -mref / scale2 per query column, so that the
+// logits come out relative to the row's fixed reference.
+template <int D>
+__device__ __forceinline__ void s_product_from(const bf16x8 (&kA)[D / 16],
+                                               const bf16x8 (&qB)[2][D / 16],
+                                               const f32x16 (&c)[2], f32x16 (&st)[2]) {
+    constexpr int KS = D / 16;
+    st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[0], qB[0][0], c[0], 0, 0, 0);
+    st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[0], qB[1][0], c[1], 0, 0, 0);
+#pragma unroll
+    for (int s = 1; s < KS; ++s) {
+        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[s], qB[0][s], st[0], 0, 0, 0);
+        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[s], qB[1][s], st[1], 0, 0, 0);
+    }
+}
+
 // Softmax, first part, for half u of tile `cur`: logits in log2 units with
 // the per-key bias, row maxima, and the (rare) rescale of the accumulators.
 // Returns in msub the reference each query half subtracts before exp2.
@@ -192,16 +212,15 @@ __device__ __forceinline__ void softmax_head(f32x16 (&st)[2], const TileRef& cur
     }
 }
 
-// Fast-path softmax, first part: logits in log2 units with the per-key bias
-// (as in softmax_head), row maxima, and the fixed reference: set by the
-// first half whose row maximum is finite, never moved afterwards.  Tracks
-// how far later row maxima rise above it; past kFixedSlack the fast path's
-// results are discarded.
+// Fast path, first half of a query block: logits in log2 units with the
+// per-key bias (as in softmax_head) and each row's maximum, which becomes
+// the row's fixed reference (-inf when the half has no finite logit for that
+// row; the caller then takes the rescaling path).
 template <int D>
-__device__ __forceinline__ void softmax_head_fixed(f32x16 (&st)[2], const TileRef& cur, int u,
-                                                   const float* srow, int half, float scale2,
-                                                   FixedState<D>& fs, float (&msub)[2]) {
-    const float* b = srow + cur.bias_off + 32 * u + 4 * half;
+__device__ __forceinline__ void first_half_reference(f32x16 (&st)[2], const TileRef& cur,
+                                                     const float* srow, int half, float scale2,
+                                                     FixedState<D>& fs) {
+    const float* b = srow + cur.bias_off + 4 * half;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const f32x4 bb = *reinterpret_cast<const f32x4*>(b + 8 * g);
@@ -216,11 +235,7 @@ __device__ __forceinline__ void softmax_head_fixed(f32x16 (&st)[2], const TileRe
         float mx = fmaxf(st[nt][0], st[nt][1]);
 #pragma unroll
         for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(st[nt][v], st[nt][v + 1]));
-        mx = max_across_halves(mx);
-        if (fs.mref[nt] == -__builtin_inff()) fs.mref[nt] = mx;
-        // (-inf - -inf is NaN, which fmaxf ignores)
-        fs.growth[nt] = fmaxf(fs.growth[nt], mx - fs.mref[nt]);
-        msub[nt] = fs.mref[nt] == -__builtin_inff() ? 0.f : fs.mref[nt];
+        fs.mref[nt] = max_across_halves(mx);
     }
 }
 
@@ -240,6 +255,29 @@ __device__ __forceinline__ void softmax_tail(const f32x16 (&st)[2], const float 
             f32x2 pp;
             pp[0] = __builtin_amdgcn_exp2f(st[nt][v] - msub[nt]);
             pp[1] = __builtin_amdgcn_exp2f(st[nt][v + 1] - msub[nt]);
+            const bf16x2 pr = __builtin_convertvector(pp, bf16x2);
+            ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
+            pB[nt][v >> 3][v & 7] = pr[0];
+            pB[nt][v >> 3][(v & 7) + 1] = pr[1];
+        }
+        rs.lsum[nt] = ps;
+    }
+}
+
+// Fast-path softmax tail: the logits are already relative to the fixed
+// reference, so P = exp2(logit) directly.
+template <typename State>
+__device__ __forceinline__ void softmax_tail_rel(const f32x16 (&st)[2], State& rs,
+                                                 bf16x8 (&pB)[2][2]) {
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        float ps = rs.lsum[nt];
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+            f32x2 pp;
+            pp[0] = __builtin_amdgcn_exp2f(st[nt][v]);
+            pp[1] = __builtin_amdgcn_exp2f(st[nt][v + 1]);
             const bf16x2 pr = __builtin_convertvector(pp, bf16x2);
             ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
             pB[nt][v >> 3][v & 7] = pr[0];
@@ -274,16 +312,16 @@ __device__ __forceinline__ void mfma_pv_acc(f32x16& acc, const bf16x8& a, const 
     asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "a"(a), "v"(b));
 }
 
-// PV of one half on the fast path with the logits, maxima and reference
-// update of the next half (softmax_head_fixed's work) spread between its
-// MFMAs by hand: the asm MFMAs are invisible to the scheduler's grouping, so
-// the order is written out and pinned with scheduling barriers.  The work
-// is cut into 16 slices: bias terms 4 at a time (slices 0-7), then the row
-// maxima, the cross-half maxima and the reference update (8-15).
+// PV of one half on the fast path with the logits and maxima of the next
+// half spread between its MFMAs by hand: the asm MFMAs are invisible to the
+// scheduler's grouping, so the order is written out and pinned with
+// scheduling barriers.  The work is cut into 16 slices: bias terms 4 at a
+// time (slices 0-7), then the row maxima, the cross-half maxima and the
+// growth above the fixed reference (8-15).  The logits are already relative
+// to the reference (the S^T accumulation started from -mref / scale2).
 template <int D>
 __device__ __forceinline__ void head_slice(int m, f32x16 (&st)[2], const f32x4 (&bb)[4],
-                                           float scale2, FixedState<D>& fs, float (&msub)[2],
-                                           float (&part)[2][2]) {
+                                           float scale2, FixedState<D>& fs, float (&part)[2][2]) {
     if (m < 8) {
         const int g = m >> 1, nt = m & 1;
 #pragma unroll
@@ -299,18 +337,14 @@ __device__ __forceinline__ void head_slice(int m, f32x16 (&st)[2], const f32x4 (
         part[nt][0] = max_across_halves(fmaxf(part[nt][0], part[nt][1]));
     } else {
         const int nt = (m - 13) >> 1;
-        const float mx = part[nt][0];
-        if (fs.mref[nt] == -__builtin_inff()) fs.mref[nt] = mx;
-        fs.growth[nt] = fmaxf(fs.growth[nt], mx - fs.mref[nt]);
-        msub[nt] = fs.mref[nt] == -__builtin_inff() ? 0.f : fs.mref[nt];
+        fs.growth[nt] = fmaxf(fs.growth[nt], part[nt][0]);  // logits relative to mref
     }
 }
 
 template <int D>
 __device__ __forceinline__ void pv_then_head(const bf16x8 (&vA)[D / 32][2], const bf16x8 (&pB)[2][2],
                                              FixedState<D>& fs, f32x16 (&st)[2], const TileRef& cur,
-                                             int u, const float* srow, int half, float scale2,
-                                             float (&msub)[2]) {
+                                             int u, const float* srow, int half, float scale2) {
     constexpr int NM = 4 * (D / 32);  // PV MFMAs of a half
     const float* b = srow + cur.bias_off + 32 * u + 4 * half;
     f32x4 bb[4];
@@ -328,7 +362,7 @@ __device__ __forceinline__ void pv_then_head(const bf16x8 (&vA)[D / 32][2], cons
                 mfma_pv_acc(fs.oacc[mt][nt], vA[mt][s], pB[nt][s]);
 #pragma unroll
                 for (int m = k * 16 / NM; m < (k + 1) * 16 / NM; ++m)
-                    head_slice<D>(m, st, bb, scale2, fs, msub, part);
+                    head_slice<D>(m, st, bb, scale2, fs, part);
                 __builtin_amdgcn_sched_barrier(0);
             }
 }
@@ -551,51 +585,61 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
         fs.mref[0] = fs.mref[1] = -__builtin_inff();
         fs.lsum[0] = fs.lsum[1] = 0.f;
         fs.growth[0] = fs.growth[1] = 0.f;
-        bf16x8 kB0[KS], kB1[KS];            // keys of even / odd halves
+        bf16x8 kB[KS];                      // keys, one half ahead
         bf16x8 vB0[MT][2], vB1[MT][2];      // values (accumulation VGPRs)
         f32x16 st0[2], st1[2];
         bf16x8 pB[2][2];
-        float msub0[2], msub1[2];
         TileRef t0 = tile_at(0);
         TileRef t1 = n_tiles > 1 ? tile_at(1) : t0;
-        // (the loads outstanding when the loop is entered are issued in the
-        // order of the loop's own, so the wait counts at the loop head hold
-        // on both paths)
-        load_k<D>(t0, 0, lane, kB0);
-        s_product<D>(kB0, qB, st0);
+        // First half: its row maxima fix the reference (a row whose first
+        // half has no finite logit -- only possible when the first tile is a
+        // pooled tile -- sends the block to the rescaling path).  Later S^T
+        // products start from -mref / scale2 so their logits come out
+        // relative to it.  (The loads outstanding when the loop is entered
+        // are issued in the order of the loop's own, so the wait counts at
+        // the loop head hold on both paths.)
+        load_k<D>(t0, 0, lane, kB);
+        s_product<D>(kB, qB, st0);
         __builtin_amdgcn_sched_barrier(0);
-        load_k<D>(t0, 1, lane, kB1);
+        load_k<D>(t0, 1, lane, kB);
         __builtin_amdgcn_sched_barrier(0);
         load_v<D>(t0, 0, lane, vB0);
         __builtin_amdgcn_sched_barrier(0);
-        load_k<D>(t1, 0, lane, kB0);
-        __builtin_amdgcn_sched_barrier(0);
-        softmax_head_fixed<D>(st0, t0, 0, srow, half, scale2, fs, msub0);
+        first_half_reference<D>(st0, t0, srow, half, scale2, fs);
+        abandoned = __ballot(fs.mref[0] == -__builtin_inff() || fs.mref[1] == -__builtin_inff()) != 0;
+        f32x16 cinit[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const float m = abandoned ? 0.f : fs.mref[nt];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                cinit[nt][v] = -m / scale2;
+                st0[nt][v] -= m;  // the first half's logits, made relative
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
 
-        // Keys are fetched two halves ahead, values one half ahead; a load
-        // phase issues the values first (they are needed first).
-        for (int t = 0; t < n_tiles; ++t) {
+        for (int t = 0; t < n_tiles && !abandoned; ++t) {
             const TileRef t2 = t + 2 < n_tiles ? tile_at(t + 2) : t1;
-            s_product<D>(kB1, qB, st1);                      // S^T (t, 1)
-            softmax_tail(st0, msub0, fs, pB);                // exp2 (t, 0)
+            s_product_from<D>(kB, qB, cinit, st1);           // S^T (t, 1)
+            softmax_tail_rel(st0, fs, pB);                   // exp2 (t, 0)
             interleave<16, 6>();
+            __builtin_amdgcn_sched_barrier(0);
+            load_k<D>(t1, 0, lane, kB);
             __builtin_amdgcn_sched_barrier(0);
             load_v<D>(t0, 1, lane, vB1);
             __builtin_amdgcn_sched_barrier(0);
-            load_k<D>(t1, 1, lane, kB1);
+            pv_then_head<D>(vB0, pB, fs, st1, t0, 1, srow, half, scale2);  // PV (t, 0)
             __builtin_amdgcn_sched_barrier(0);
-            pv_then_head<D>(vB0, pB, fs, st1, t0, 1, srow, half, scale2, msub1);  // PV (t, 0)
-            __builtin_amdgcn_sched_barrier(0);
-            s_product<D>(kB0, qB, st0);                      // S^T (t+1, 0)
-            softmax_tail(st1, msub1, fs, pB);                // exp2 (t, 1)
+            s_product_from<D>(kB, qB, cinit, st0);           // S^T (t+1, 0)
+            softmax_tail_rel(st1, fs, pB);                   // exp2 (t, 1)
             interleave<16, 6>();
+            __builtin_amdgcn_sched_barrier(0);
+            load_k<D>(t1, 1, lane, kB);
             __builtin_amdgcn_sched_barrier(0);
             load_v<D>(t1, 0, lane, vB0);
             __builtin_amdgcn_sched_barrier(0);
-            load_k<D>(t2, 0, lane, kB0);
-            __builtin_amdgcn_sched_barrier(0);
-            pv_then_head<D>(vB1, pB, fs, st0, t1, 0, srow, half, scale2, msub0);  // PV (t, 1)
+            pv_then_head<D>(vB1, pB, fs, st0, t1, 0, srow, half, scale2);  // PV (t, 1)
             __builtin_amdgcn_sched_barrier(0);
             t0 = t1;
             t1 = t2;
@@ -603,7 +647,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
         // (the loop runs to its end even when some row rose past its
         // reference -- inf or NaN may then have reached the accumulators --
         // and the results are discarded here)
-        abandoned = __ballot(fmaxf(fs.growth[0], fs.growth[1]) > kFixedSlack) != 0;
+        abandoned = abandoned || __ballot(fmaxf(fs.growth[0], fs.growth[1]) > kFixedSlack) != 0;
         acc_fence();
         if (!abandoned) store_rows<D>(fs.oacc, fs.lsum, op, i, N, half, l32);
     }
