@@ -88,3 +88,38 @@ def test_draft_workload_calibrated_tau():
 def test_long_workload_ragged_tail():
     m = run_workload("long", 5000, 1.5, heads=(0, 31), block_step=40)
     assert m.shape[-1] == 757
+
+
+@pytest.mark.parametrize("mode,tau", [("sparse", 1.25), ("topk", 0.1), ("dense", 0.0)])
+def test_maximum_sequence_length(mode, tau):
+    # N = 64 * 4096 = 262144 tokens, the largest the library accepts (4096
+    # key blocks: the longest LDS score row and kept list); one head, d = 128,
+    # bf16, field inputs with a 2048-token prefix.  Masks on sampled query
+    # blocks against the oracle's routing, outputs on a few of them.
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    N, prefix = 64 * 4096, 2048
+    q, k, v = inputs.custom(1, 1, N, 128, "bf16", prefix_len=prefix, seed=61, kind="field",
+                            grid=(256, 32, 32))
+    qd, kd, vd = device_tensors(q, k, v, "bf16")
+    out, words, _, thr = sa.solattn_forward_debug(qd, kd, vd, None, prefix, tau, mode,
+                                                  want_scores=False)
+    torch.cuda.synchronize()
+    nb = N // 64
+    gmask = sa.unpack_mask(words, nb)
+    blocks = [0, 1, 31, 32, 1000, 2047, 3000, nb - 1]
+    omode = {"sparse": oracle.SPARSE, "topk": oracle.TOPK, "dense": oracle.DENSE}[mode]
+    otau = float(np.float32(tau))
+    r = oracle.head(q[0, 0], k[0, 0], v[0, 0], prefix, otau, mode=omode, qblocks=blocks,
+                    want_out=False)
+    for i in blocks:
+        om = r["mask"][i].astype(bool)
+        near = np.abs(r["score"][i] - r["thr"][i]) <= 1e-4 if mode != "dense" else np.zeros(nb, bool)
+        assert not ((gmask[0, 0, i] != om) & ~near).any(), i
+    sample = [0, 1000, nb - 1]
+    ro = oracle.head(q[0, 0], k[0, 0], v[0, 0], prefix, otau, mode=omode,
+                     mask_override=gmask[0, 0].astype(np.uint8), qblocks=sample)
+    ab, _ = out_error(out[0, 0].float().cpu().numpy().astype(np.float64), ro["out"],
+                      block_rows(sample, N))
+    print("max N %s: kept blocks/row %.1f, max abs err %.4g" % (mode, gmask[0, 0, blocks].sum(-1).mean(), ab))
+    assert ab <= TOL_BF16_ABS
