@@ -17,9 +17,9 @@
 //   * each 64-key tile is consumed as two 32-key halves in a software
 //     pipeline whose phases pair matrix-core and vector work: the S^T
 //     products of half h+1 run beside the exp2 work of half h, and the PV
-//     products of half h beside the logits and maxima of half h+1, with
-//     the MFMAs and vector instructions interleaved one by one.  Keys are
-//     prefetched into registers two halves ahead, values one half ahead;
+//     products of half h beside the logits of half h+1, with the MFMAs and
+//     vector instructions interleaved one by one.  Keys are prefetched into
+//     registers two halves ahead, values one half ahead;
 //   * one wave per SIMD: the 64 x d fp32 output accumulator and the value
 //     buffers live in the accumulation VGPRs (the PV MFMAs are inline asm),
 //     the arch VGPRs hold Q^T, S^T, P and the key buffers;
@@ -33,10 +33,13 @@
 //     rescales: weights up to 2^64 above it stay far from the fp32/bf16
 //     range limit.  Every later S^T accumulation starts from -mref/scale2
 //     instead of zero, so its logits come out relative to the reference and
-//     the exp2 needs no subtraction.  If some row's first half has no
-//     finite logit, or some row's maximum later rose more than 2^64 above
-//     the reference, the fast path's result is discarded and the query
-//     block is recomputed from the start by the rescaling path (VGPR
+//     the exp2 needs no subtraction.  No row maximum is tracked after the
+//     first half: a row whose logits later rose more than 64 above the
+//     reference has a weight, and so a denominator, above 2^64, and that
+//     is checked once at the end.  If some row's first half has no finite
+//     logit, or some denominator ends above 2^64 (or inf / NaN), the fast
+//     path's result is discarded and the query block is recomputed from
+//     the start by the rescaling path (VGPR
 //     accumulators, lazy rescale when the maximum grows by more than 2^8).  The denominator adds the
 //     bf16-rounded weights the MFMA consumes (v_dot2 against (1, 1)), so
 //     numerator and denominator agree;
@@ -52,7 +55,10 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;   // rescaling path: lazy-rescale margin (log2)
-constexpr float kFixedSlack = 64.0f;    // fast path: growth over the fixed reference (log2)
+// Fast path: largest denominator share a lane may end with (2^64).  Every
+// weight is at most its row's denominator, so a row whose logits rose more
+// than 64 (log2 units) above the fixed reference ends above it.
+constexpr float kFixedSumMax = 18446744073709551616.0f;
 
 // One 64-key tile of the sequence: an exact key block or a pooled tile.
 struct TileRef {
@@ -127,7 +133,6 @@ struct FixedState {
     f32x16 oacc[D / 32][2];
     float mref[2];
     float lsum[2];
-    float growth[2];  // largest row maximum seen above the reference
 };
 
 // S^T = K Q^T for one 32-key half: 32 keys x 64 queries, two 32x32
@@ -312,33 +317,17 @@ __device__ __forceinline__ void mfma_pv_acc(f32x16& acc, const bf16x8& a, const 
     asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "a"(a), "v"(b));
 }
 
-// PV of one half on the fast path with the logits and maxima of the next
-// half spread between its MFMAs by hand: the asm MFMAs are invisible to the
-// scheduler's grouping, so the order is written out and pinned with
-// scheduling barriers.  The work is cut into 16 slices: bias terms 4 at a
-// time (slices 0-7), then the row maxima, the cross-half maxima and the
-// growth above the fixed reference (8-15).  The logits are already relative
-// to the reference (the S^T accumulation started from -mref / scale2).
-template <int D>
+// PV of one half on the fast path with the logits of the next half (log2
+// units plus the per-key bias) spread between its MFMAs by hand: the asm
+// MFMAs are invisible to the scheduler's grouping, so the order is written
+// out and pinned with scheduling barriers.  Slice m of 16 handles two of
+// the 32 values a lane holds.  The logits are already relative to the
+// reference (the S^T accumulation started from -mref / scale2).
 __device__ __forceinline__ void head_slice(int m, f32x16 (&st)[2], const f32x4 (&bb)[4],
-                                           float scale2, FixedState<D>& fs, float (&part)[2][2]) {
-    if (m < 8) {
-        const int g = m >> 1, nt = m & 1;
+                                           float scale2) {
+    const int g = m >> 2, nt = (m >> 1) & 1, r0 = (m & 1) * 2;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st[nt][4 * g + r] = st[nt][4 * g + r] * scale2 + bb[g][r];
-    } else if (m < 12) {
-        const int nt = (m - 8) >> 1, h8 = ((m - 8) & 1) * 8;
-        float mx = fmaxf(st[nt][h8], st[nt][h8 + 1]);
-#pragma unroll
-        for (int v = 2; v < 8; v += 2) mx = fmaxf(mx, fmaxf(st[nt][h8 + v], st[nt][h8 + v + 1]));
-        part[nt][(m - 8) & 1] = mx;
-    } else if (m == 12 || m == 14) {
-        const int nt = (m - 12) >> 1;
-        part[nt][0] = max_across_halves(fmaxf(part[nt][0], part[nt][1]));
-    } else {
-        const int nt = (m - 13) >> 1;
-        fs.growth[nt] = fmaxf(fs.growth[nt], part[nt][0]);  // logits relative to mref
-    }
+    for (int r = r0; r < r0 + 2; ++r) st[nt][4 * g + r] = st[nt][4 * g + r] * scale2 + bb[g][r];
 }
 
 template <int D>
@@ -350,7 +339,6 @@ __device__ __forceinline__ void pv_then_head(const bf16x8 (&vA)[D / 32][2], cons
     f32x4 bb[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) bb[g] = *reinterpret_cast<const f32x4*>(b + 8 * g);
-    float part[2][2];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -362,7 +350,7 @@ __device__ __forceinline__ void pv_then_head(const bf16x8 (&vA)[D / 32][2], cons
                 mfma_pv_acc(fs.oacc[mt][nt], vA[mt][s], pB[nt][s]);
 #pragma unroll
                 for (int m = k * 16 / NM; m < (k + 1) * 16 / NM; ++m)
-                    head_slice<D>(m, st, bb, scale2, fs, part);
+                    head_slice(m, st, bb, scale2);
                 __builtin_amdgcn_sched_barrier(0);
             }
 }
@@ -568,11 +556,11 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     // loads that the in-order vmcnt waits rely on, in place):
     //   S^T of half h+1 beside the exp2 work of half h;
     //   loads of the values of half h+1, then of the keys of half h+3;
-    //   PV of half h with the logits, maxima and bias of half h+1 placed
+    //   PV of half h with the logits (scale and bias) of half h+1 placed
     //   between its MFMAs by hand (pv_then_head).
     // Past the end the prefetches and the S^T products re-read the last tile
     // (their results are never used), so every iteration runs the same
-    // straight-line code; a repeated half cannot raise a row's maximum.
+    // straight-line code.
     bool abandoned = false;
     {
         FixedState<D> fs;
@@ -584,8 +572,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
                 for (int v = 0; v < 16; ++v) fs.oacc[mt][nt][v] = 0.f;
         fs.mref[0] = fs.mref[1] = -__builtin_inff();
         fs.lsum[0] = fs.lsum[1] = 0.f;
-        fs.growth[0] = fs.growth[1] = 0.f;
-        bf16x8 kB[KS];                      // keys, one half ahead
+        bf16x8 kB0[KS], kB1[KS];            // keys of even / odd halves
         bf16x8 vB0[MT][2], vB1[MT][2];      // values (accumulation VGPRs)
         f32x16 st0[2], st1[2];
         bf16x8 pB[2][2];
@@ -598,12 +585,15 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
         // relative to it.  (The loads outstanding when the loop is entered
         // are issued in the order of the loop's own, so the wait counts at
         // the loop head hold on both paths.)
-        load_k<D>(t0, 0, lane, kB);
-        s_product<D>(kB, qB, st0);
+        load_k<D>(t0, 0, lane, kB0);
         __builtin_amdgcn_sched_barrier(0);
-        load_k<D>(t0, 1, lane, kB);
+        load_k<D>(t0, 1, lane, kB1);
         __builtin_amdgcn_sched_barrier(0);
         load_v<D>(t0, 0, lane, vB0);
+        __builtin_amdgcn_sched_barrier(0);
+        s_product<D>(kB0, qB, st0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_k<D>(t1, 0, lane, kB0);
         __builtin_amdgcn_sched_barrier(0);
         first_half_reference<D>(st0, t0, srow, half, scale2, fs);
         abandoned = __ballot(fs.mref[0] == -__builtin_inff() || fs.mref[1] == -__builtin_inff()) != 0;
@@ -619,35 +609,41 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
 
+        // Values are loaded one phase pair ahead of their PV product, keys
+        // two (each key buffer is refilled right after its S^T product), and
+        // each value load is issued before the key load of the same phase so
+        // that waiting for the values does not wait for the keys.
         for (int t = 0; t < n_tiles && !abandoned; ++t) {
             const TileRef t2 = t + 2 < n_tiles ? tile_at(t + 2) : t1;
-            s_product_from<D>(kB, qB, cinit, st1);           // S^T (t, 1)
+            s_product_from<D>(kB1, qB, cinit, st1);          // S^T (t, 1)
             softmax_tail_rel(st0, fs, pB);                   // exp2 (t, 0)
             interleave<16, 6>();
             __builtin_amdgcn_sched_barrier(0);
-            load_k<D>(t1, 0, lane, kB);
-            __builtin_amdgcn_sched_barrier(0);
             load_v<D>(t0, 1, lane, vB1);
+            __builtin_amdgcn_sched_barrier(0);
+            load_k<D>(t1, 1, lane, kB1);
             __builtin_amdgcn_sched_barrier(0);
             pv_then_head<D>(vB0, pB, fs, st1, t0, 1, srow, half, scale2);  // PV (t, 0)
             __builtin_amdgcn_sched_barrier(0);
-            s_product_from<D>(kB, qB, cinit, st0);           // S^T (t+1, 0)
+            s_product_from<D>(kB0, qB, cinit, st0);          // S^T (t+1, 0)
             softmax_tail_rel(st1, fs, pB);                   // exp2 (t, 1)
             interleave<16, 6>();
             __builtin_amdgcn_sched_barrier(0);
-            load_k<D>(t1, 1, lane, kB);
-            __builtin_amdgcn_sched_barrier(0);
             load_v<D>(t1, 0, lane, vB0);
+            __builtin_amdgcn_sched_barrier(0);
+            load_k<D>(t2, 0, lane, kB0);
             __builtin_amdgcn_sched_barrier(0);
             pv_then_head<D>(vB1, pB, fs, st0, t1, 0, srow, half, scale2);  // PV (t, 1)
             __builtin_amdgcn_sched_barrier(0);
             t0 = t1;
             t1 = t2;
         }
-        // (the loop runs to its end even when some row rose past its
+        // (the loop runs to its end even when some row rose far past its
         // reference -- inf or NaN may then have reached the accumulators --
-        // and the results are discarded here)
-        abandoned = abandoned || __ballot(fmaxf(fs.growth[0], fs.growth[1]) > kFixedSlack) != 0;
+        // and the results are discarded here; a NaN denominator fails the
+        // comparison and is discarded too)
+        abandoned = abandoned ||
+                    __ballot(!(fs.lsum[0] <= kFixedSumMax && fs.lsum[1] <= kFixedSumMax)) != 0;
         acc_fence();
         if (!abandoned) store_rows<D>(fs.oacc, fs.lsum, op, i, N, half, l32);
     }

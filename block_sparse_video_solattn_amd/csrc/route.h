@@ -76,19 +76,30 @@ __device__ inline RouteResult route_query_block(const AttnArgs& a, int64_t bh, i
     // load instruction reads 1 KiB of consecutive key blocks.
     const float* __restrict__ qb = a.qbar + (bh * Nb + i) * D;
     const float* __restrict__ kt = a.kbarT + bh * D * Nbp;
-    // (loads are issued in batches of 64 rows of kbarT before their FMAs so
-    // that the wave waits for memory about twice per 256 key blocks instead
-    // of once per few rows; the accumulation order over d is unchanged)
-    constexpr int DB = D < 64 ? D : 64;
+    // (rows of kbarT are loaded in batches of DB, DEPTH batches in flight:
+    // the loads of batch b + DEPTH - 1 are issued before the FMAs of batch
+    // b, so that the wave's memory latency is paid about once per 256 key
+    // blocks rather than once per batch; the accumulation order over d is
+    // plain ascending d)
+    constexpr int DB = 16, NB = D / DB, DEPTH = 3;
     for (int64_t j0 = 4 * lane; j0 < Nbp; j0 += 256) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int d0 = 0; d0 < D; d0 += DB) {
-            f32x4 kv[DB];
+        f32x4 kv[DEPTH][DB];
+#pragma unroll
+        for (int b = 0; b < DEPTH - 1; ++b)
 #pragma unroll
             for (int d = 0; d < DB; ++d)
-                kv[d] = *reinterpret_cast<const f32x4*>(kt + (int64_t)(d0 + d) * Nbp + j0);
+                kv[b][d] = *reinterpret_cast<const f32x4*>(kt + (int64_t)(b * DB + d) * Nbp + j0);
 #pragma unroll
-            for (int d = 0; d < DB; ++d) acc += qb[d0 + d] * kv[d];
+        for (int b = 0; b < NB; ++b) {
+            if (b + DEPTH - 1 < NB) {
+#pragma unroll
+                for (int d = 0; d < DB; ++d)
+                    kv[(b + DEPTH - 1) % DEPTH][d] = *reinterpret_cast<const f32x4*>(
+                        kt + (int64_t)((b + DEPTH - 1) * DB + d) * Nbp + j0);
+            }
+#pragma unroll
+            for (int d = 0; d < DB; ++d) acc += qb[b * DB + d] * kv[b % DEPTH][d];
         }
         *reinterpret_cast<f32x4*>(srow + j0) = acc * scale;
     }
