@@ -21,6 +21,7 @@ METRIC = "ms/call + dense-equiv TFLOP/s and % bf16 MFMA peak on kept tiles, N=16
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
 SEED = 3000
+SEED_LONG = 5000
 
 # HBM traffic of one attention dispatch from rocprofv3 counters on this
 # workload: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), scaled by what the
@@ -149,6 +150,75 @@ def draft_check(sa, stream):
                                   "speedup_vs_dense": round(dms / tms, 2)}}
 
 
+def pool_bytes(B, H, N, d):
+    """Algorithmic HBM bytes of one packing pass of the pooling kernel: per
+    (slice, 64-token block) 3*64*d bf16 elements read; written: the fp32
+    means of q, k and v, the fp32 transposed key mean, the bf16 pooled key
+    and value operands and the bf16 operand-ordered 64 x d key and value
+    tiles (384*d read + 276*d written bytes per block)."""
+    nb = (N + 63) // 64
+    return B * H * nb * (384 + 276) * d
+
+
+def long_clip_check(sa, stream):
+    """The long-clip stress shape (2048 packed prefix + 46368 video tokens,
+    tau = 1.5): sparsity, pooling bandwidth, routing setup time and the
+    attention kernel's kept-tile rate, timed in the same run."""
+    import numpy as np
+    import torch
+    from block_sparse_video_solattn_amd import inputs
+    w = inputs.WORKLOADS["long"]
+    tau = w.taus[0]
+    log("generating long-clip inputs (B=%d H=%d N=%d d=%d)" % (w.B, w.H, w.N, w.D))
+    q, k, v = inputs.make_inputs(w, SEED_LONG)
+    qd, kd, vd = [torch.from_numpy(x).to("cuda").to(torch.bfloat16).contiguous() for x in (q, k, v)]
+    del q, k, v
+    out = torch.empty_like(qd)
+    ws = torch.empty(sa.solattn_workspace_bytes(w.B, w.H, w.N, w.D, sa.BF16), dtype=torch.uint8,
+                     device="cuda")
+    words, _, _ = sa.solattn_route(qd, kd, vd, w.prefix_len, tau, want_scores=False)
+    torch.cuda.synchronize()
+    m = sa.unpack_mask(words, w.nb)
+    fk, fp = kept_flops(m, w.N, w.D)
+    pb = (w.prefix_len + 63) // 64
+
+    def prep():
+        sa.solattn_prepare_ws(qd, kd, vd, "sparse", ws)
+
+    def attend():
+        sa.solattn_attend_ws(qd, kd, vd, out, w.prefix_len, tau, "sparse", ws)
+
+    def call():
+        prep()
+        attend()
+    for _ in range(3):
+        call()
+    cms = float(np.median(time_calls(call, 10, stream)))
+    pms = float(np.median(time_calls(prep, 10, stream)))
+    prep()
+    ams = float(np.median(time_calls(attend, 10, stream)))
+    mw = torch.zeros((w.B, w.H, w.nb, (w.nb + 31) // 32), dtype=torch.int32, device="cuda")
+    th = torch.zeros((w.B, w.H, w.nb), dtype=torch.float32, device="cuda")
+
+    def setup():
+        sa.solattn_route(qd, kd, vd, w.prefix_len, tau, want_scores=False, mask=mw, thr=th)
+    setup()
+    sms = float(np.median(time_calls(setup, 10, stream)))
+    tflops = fk / (ams * 1e-3) / 1e12
+    return {"workload": "long clip: 15 s at 1344x768 -> 46x24x42 latent, 2048 prefix + 46368 "
+                        "video tokens", "N": w.N, "tau": tau,
+            "video_sparsity": round(float(1 - m[..., pb:].mean()), 4),
+            "ms_per_call": round(cms, 4),
+            "dense_equiv_tflops": round(4.0 * w.B * w.H * w.N * w.N * w.D / (cms * 1e-3) / 1e12, 1),
+            "pool_ms": round(pms, 4),
+            "pool_GBps": round(pool_bytes(w.B, w.H, w.N, w.D) / (pms * 1e-3) / 1e9, 1),
+            "setup_ms": round(sms, 4),
+            "attn_ms": round(ams, 4),
+            "kept_tile_tflop": round(fk / 1e12, 4), "pooled_tflop": round(fp / 1e12, 5),
+            "attn_kept_tflops": round(tflops, 1),
+            "attn_kept_mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +325,7 @@ def main():
         "pool_ms": round(pool_ms, 4),
         "attn_ms": round(attn_ms, 4),
         "pool_read_GBps": round(pool_read / (pool_ms * 1e-3) / 1e9, 1),
+        "pool_GBps": round(pool_bytes(B, H, N, d) / (pool_ms * 1e-3) / 1e9, 1),
         "video_block_sparsity": round(video_skip, 4),
         "kept_tile_tflop": round(fk / 1e12, 4),
         "pooled_tflop": round(fp / 1e12, 5),
@@ -312,6 +383,8 @@ def main():
         del qd, kd, vd, out, ws, dev
         torch.cuda.empty_cache()
         res["sparsity_90_check"] = draft_check(sa, stream)
+        torch.cuda.empty_cache()
+        res["long_clip"] = long_clip_check(sa, stream)
 
     if not args.no_cpu:
         log("timing the CPU oracle baseline")
