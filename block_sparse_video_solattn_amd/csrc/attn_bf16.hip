@@ -487,29 +487,18 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     uint16_t* klist = reinterpret_cast<uint16_t*>(smem + Nbp + 128);
     uint16_t* plist = reinterpret_cast<uint16_t*>(smem + Nbp + 128 + (Nb + 15) / 16 * 8);
 
-    int n_kept;
-    uint64_t tile_mask;
-    if (a.mode != kDense) {
-        const RouteResult r = route_query_block<D>(a, bh, i, srow, klist);
-        n_kept = r.n_kept;
-        tile_mask = r.tile_mask;
-    } else {
-        export_dense_route(a, bh, i);
-        n_kept = (int)Nb;
-        tile_mask = 0;
-    }
-
     const bf16* qp = reinterpret_cast<const bf16*>(a.q) + bh * N * D;
     const bf16* kp = reinterpret_cast<const bf16*>(a.kP) + bh * Nb * D * 64;
     const bf16* vp = reinterpret_cast<const bf16*>(a.vP) + bh * Nb * D * 64;
     const bf16* kbp = reinterpret_cast<const bf16*>(a.kbarP) + bh * Nbp * D;
     const bf16* vbp = reinterpret_cast<const bf16*>(a.vbarP) + bh * Nbp * D;
     const int tail = (int)(N - (Nb - 1) * 64);  // keys in the last block (1..64)
-    srow[zero_bias + lane] = 0.f;
-    srow[tail_bias + lane] = lane < tail ? 0.f : -__builtin_inff();
 
     // Q^T as the B operand of S^T = K Q^T, held in registers for the whole
-    // query block: lane holds query 32*nt + l32, d = 16*s + 8*half .. +7
+    // query block: lane holds query 32*nt + l32, d = 16*s + 8*half .. +7.
+    // Loaded between the two parts of the routing, so that the block's trip
+    // from HBM overlaps the threshold and keep-mask work.
+    if (a.mode != kDense) route_scores<D>(a, bh, i, srow);
     bf16x8 qB[2][KS];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -519,6 +508,19 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) qB[nt][s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
     }
+    int n_kept;
+    uint64_t tile_mask;
+    if (a.mode != kDense) {
+        const RouteResult r = route_select(a, bh, i, srow, klist);
+        n_kept = r.n_kept;
+        tile_mask = r.tile_mask;
+    } else {
+        export_dense_route(a, bh, i);
+        n_kept = (int)Nb;
+        tile_mask = 0;
+    }
+    srow[zero_bias + lane] = 0.f;
+    srow[tail_bias + lane] = lane < tail ? 0.f : -__builtin_inff();
     __syncthreads();
 
     const float scale2 = kLog2e / sqrtf((float)D);

@@ -55,10 +55,29 @@ __host__ __device__ inline int ktile_offset(int KS, int u, int s, int lane, int 
 // Round-to-nearest-even fp32 -> bf16 (finite inputs).
 __device__ inline bf16 to_bf16(float x) { return (bf16)x; }
 
+// Sum over the 64 lanes, the same bits in every lane, without LDS round
+// trips: pairs within quads, quads within 8 lanes, 8-lane groups within
+// rows of 16 (DPP quad_perm, row_half_mirror, row_mirror), then rows 0+1 /
+// 2+3 and the two halves (v_permlane16_swap, v_permlane32_swap).  Every
+// step adds two values that the partner lane adds in the other order, so
+// all lanes hold bit-identical partial sums throughout.
+template <int CTRL>
+__device__ inline float dpp_add(float x) {
+    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false);
+    return x + __int_as_float(y);
+}
+
 __device__ inline float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+    x = dpp_add<0xb1>(x);   // quad_perm [1, 0, 3, 2]
+    x = dpp_add<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+    x = dpp_add<0x141>(x);  // row_half_mirror
+    x = dpp_add<0x140>(x);  // row_mirror
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                      false);
+    x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                      false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 __device__ inline float wave_max(float x) {

@@ -61,13 +61,13 @@ struct RouteResult {
                          // holds at least one skipped block
 };
 
-// One wavefront (all 64 lanes of the workgroup).  On return:
-//   klist[0..n_kept)  kept key-block indices (ascending)
-//   srow[0..Nbp)      log2(n_j) for skipped blocks, -inf for kept and padding
-//                     (the per-column bias of the pooled tiles, log2 units)
+// Routing in two parts, so that a caller can issue other memory loads
+// between them (route_scores waits for all of its own loads; route_select
+// issues none).  One wavefront (all 64 lanes of the workgroup).
+//
+// route_scores: srow[0..Nbp) = s_ij for every key block j (padding: 0).
 template <int D>
-__device__ inline RouteResult route_query_block(const AttnArgs& a, int64_t bh, int64_t i,
-                                                float* srow, uint16_t* klist) {
+__device__ inline void route_scores(const AttnArgs& a, int64_t bh, int64_t i, float* srow) {
     const int lane = threadIdx.x & 63;
     const int64_t Nb = a.Nb, Nbp = a.Nbp;
     const float scale = 1.0f / sqrtf((float)D);
@@ -104,7 +104,16 @@ __device__ inline RouteResult route_query_block(const AttnArgs& a, int64_t bh, i
         *reinterpret_cast<f32x4*>(srow + j0) = acc * scale;
     }
     __syncthreads();
+}
 
+// route_select, from the scores in srow.  On return:
+//   klist[0..n_kept)  kept key-block indices (ascending)
+//   srow[0..Nbp)      log2(n_j) for skipped blocks, -inf for kept and padding
+//                     (the per-column bias of the pooled tiles, log2 units)
+__device__ inline RouteResult route_select(const AttnArgs& a, int64_t bh, int64_t i, float* srow,
+                                           uint16_t* klist) {
+    const int lane = threadIdx.x & 63;
+    const int64_t Nb = a.Nb, Nbp = a.Nbp;
     float thr;
     if (a.mode == kTopk) {
         thr = kth_largest_video(srow, a.Pb, Nb, a.topk);
@@ -127,16 +136,19 @@ __device__ inline RouteResult route_query_block(const AttnArgs& a, int64_t bh, i
             thr = mu + a.tau * sigma;
     }
 
-    // keep bits, kept list, pooled-tile flags, pooled biases
+    // keep bits, kept list, pooled-tile flags, pooled biases (log2 n_j: 6
+    // for a full block, log2 of its key count for a ragged last block)
     int n_kept = 0;
     uint64_t tile_mask = 0;
     const int64_t W = (Nb + 31) / 32;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int64_t j0 = 0; j0 < Nbp; j0 += 64) {
-        const int64_t j = j0 + lane;
-        const bool valid = j < Nb;
+    const int nb = (int)Nb, nbp = (int)Nbp, pb = (int)a.Pb;
+    const float log2_last = log2f((float)(a.N - (Nb - 1) * 64));
+    for (int j0 = 0; j0 < nbp; j0 += 64) {
+        const int j = j0 + lane;
+        const bool valid = j < nb;
         const float s = srow[j];
-        const bool keep = valid && (j < a.Pb || s >= thr);
+        const bool keep = valid && (j < pb || s >= thr);
         const bool skip = valid && !keep;
         const uint64_t kb = __ballot(keep);
         const uint64_t sb = __ballot(skip);
@@ -149,12 +161,18 @@ __device__ inline RouteResult route_query_block(const AttnArgs& a, int64_t bh, i
         if (keep) klist[n_kept + __popcll(kb & lt)] = (uint16_t)j;
         n_kept += __popcll(kb);
         if (sb && a.mode == kSparse) tile_mask |= 1ull << (j0 / 64);  // pooled terms: Sol-Attn only
-        const int nj = (int)((j + 1) * 64 <= a.N ? 64 : a.N - j * 64);
-        srow[j] = skip ? log2f((float)nj) : -__builtin_inff();
+        srow[j] = skip ? (j == nb - 1 ? log2_last : 6.0f) : -__builtin_inff();
     }
     if (a.thr_out && lane == 0) a.thr_out[bh * Nb + i] = thr;
     __syncthreads();
     return RouteResult{n_kept, tile_mask};
+}
+
+template <int D>
+__device__ inline RouteResult route_query_block(const AttnArgs& a, int64_t bh, int64_t i,
+                                                float* srow, uint16_t* klist) {
+    route_scores<D>(a, bh, i, srow);
+    return route_select(a, bh, i, srow, klist);
 }
 
 // Dense mode exports: every bit set, threshold -inf.

@@ -123,3 +123,22 @@ def test_maximum_sequence_length(mode, tau):
                       block_rows(sample, N))
     print("max N %s: kept blocks/row %.1f, max abs err %.4g" % (mode, gmask[0, 0, blocks].sum(-1).mean(), ab))
     assert ab <= TOL_BF16_ABS
+
+
+@pytest.mark.parametrize("mode,tau", [("sparse", 1.25), ("dense", 0.0)])
+def test_attend_repeated_after_one_prepare(mode, tau):
+    # Repeated attention launches after one pooling launch read the same
+    # workspace and must give the forward pass's output bit for bit (nothing
+    # the attention kernel leaves behind may change the next launch).
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    w, q, k, v, (qd, kd, vd) = workload_inputs("refine", 3000)
+    ref = sa.solattn_forward(qd, kd, vd, None, w.prefix_len, tau, mode)
+    ws = torch.empty(sa.solattn_workspace_bytes(w.B, w.H, w.N, w.D, sa.BF16), dtype=torch.uint8,
+                     device="cuda")
+    sa.solattn_prepare_ws(qd, kd, vd, mode, ws)
+    for rep in range(3):
+        out = torch.full_like(qd, float("nan"))
+        sa.solattn_attend_ws(qd, kd, vd, out, w.prefix_len, tau, mode, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep
