@@ -21,6 +21,9 @@ _LIB = os.path.join(_HERE, "libsolattn_oracle.so")
 _lib = None
 
 DENSE, SPARSE, TOPK = 0, 1, 2
+# routing variants, added to SPARSE (both) or TOPK (PREFIX_ROWS): prefix query
+# blocks keep every key block; threshold statistics over the video key blocks
+PREFIX_ROWS, VIDEO_STATS = 0x10, 0x20
 BLOCK = 64
 
 

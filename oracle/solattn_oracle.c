@@ -52,6 +52,19 @@
  * kept).  The pages do not say how the draft picks its blocks; ranking by the
  * same pooled score is the reading taken.  Skipped blocks contribute nothing
  * (plain block-sparse attention, no pooled term).
+ *
+ * Two routing variants, as flag bits added to the mode (other readings of
+ * passages the main reading resolves one way):
+ *   PREFIX_ROWS (0x10, with SPARSE or TOPK): the prefix takes exact
+ *     attention on the query side too -- query blocks i < Pb keep every key
+ *     block (thr_i = -inf).  Page "英伟达开源 Sol-H3", section 2.2, says the
+ *     packed prefix always takes exact attention without naming a side.
+ *   VIDEO_STATS (0x20, with SPARSE): mu_i and sigma_i are taken over the
+ *     video key blocks j >= Pb only (the prefix blocks are kept anyway); a
+ *     row with no video block has thr_i = +inf.  Page "MiniMax 官宣 ...",
+ *     section "提速来自流水线每一段的叠加", speaks of the query block's own
+ *     score statistics without saying whether the always-kept prefix enters
+ *     them.
  */
 #include <math.h>
 #include <stdint.h>
@@ -64,6 +77,7 @@
 #define ORACLE_BLOCK 64
 
 enum { ORACLE_DENSE = 0, ORACLE_SPARSE = 1, ORACLE_TOPK = 2 };
+enum { ORACLE_BASE_MASK = 0x0f, ORACLE_PREFIX_ROWS = 0x10, ORACLE_VIDEO_STATS = 0x20 };
 
 /* Number of tokens in block j. */
 static int64_t block_len(int64_t N, int64_t j) {
@@ -92,15 +106,19 @@ static void pool_blocks(const double* x, int64_t N, int64_t d, double* xbar) {
     }
 }
 
-/* Step 4 for one query block: threshold of a score row. */
-static double row_threshold(const double* s, int64_t Nb, double tau) {
+/* Step 4 for one query block: threshold of a score row, with the statistics
+ * taken over the blocks [lo, Nb) (lo = 0: the whole row; lo = Pb: the video
+ * blocks; +inf when that range is empty). */
+static double row_threshold(const double* s, int64_t lo, int64_t Nb, double tau) {
     if (isinf(tau)) return tau;  /* -inf keeps all, +inf keeps only the prefix */
+    if (lo >= Nb) return INFINITY;
+    const double n = (double)(Nb - lo);
     double mu = 0.0;
-    for (int64_t j = 0; j < Nb; ++j) mu += s[j];
-    mu /= (double)Nb;
+    for (int64_t j = lo; j < Nb; ++j) mu += s[j];
+    mu /= n;
     double var = 0.0;
-    for (int64_t j = 0; j < Nb; ++j) var += (s[j] - mu) * (s[j] - mu);
-    double sigma = sqrt(var / (double)Nb);
+    for (int64_t j = lo; j < Nb; ++j) var += (s[j] - mu) * (s[j] - mu);
+    double sigma = sqrt(var / n);
     if (sigma == 0.0) return mu;
     return mu + tau * sigma;
 }
@@ -175,7 +193,9 @@ static void attend_row(const double* qr, const double* k, const double* v,
  * One (b, h) slice.
  *   q, k, v      [N][d] fp64.
  *   mode         0 dense, 1 sparse (Sol-Attn), 2 topk (tau = kept fraction of
- *                the video key blocks, 0 < tau <= 1; no pooled terms).
+ *                the video key blocks, 0 < tau <= 1; no pooled terms), plus
+ *                the flags PREFIX_ROWS (0x10, sparse or topk) and
+ *                VIDEO_STATS (0x20, sparse).
  *   mask_override [Nb][Nb] keep bits (0/1) or NULL; when given it is used
  *                as is (no prefix forcing) in either mode.
  *   qblocks      list of query blocks to produce, or NULL for all of them.
@@ -184,8 +204,8 @@ static void attend_row(const double* qr, const double* k, const double* v,
  *                or NULL: rows of the listed query blocks are written.
  *   qbar_out, kbar_out, vbar_out  [Nb][d] or NULL (all blocks).
  * Returns 0, or -1 for invalid arguments (d < 1, N < 1, prefix_len outside
- * [0, N], NaN tau, unknown mode, topk fraction outside (0, 1]), or -2 when
- * memory runs out.
+ * [0, N], NaN tau, unknown mode or flag, a flag its mode does not take, topk
+ * fraction outside (0, 1]), or -2 when memory runs out.
  */
 int solattn_oracle_head(const double* q, const double* k, const double* v,
                         int64_t N, int64_t d, int64_t prefix_len, double tau, int mode,
@@ -193,9 +213,14 @@ int solattn_oracle_head(const double* q, const double* k, const double* v,
                         int64_t n_qblocks, double* out, uint8_t* mask_out,
                         double* score_out, double* thr_out, double* qbar_out,
                         double* kbar_out, double* vbar_out, int threads) {
+    const int flags = mode & ~ORACLE_BASE_MASK;
+    mode &= ORACLE_BASE_MASK;
     if (!q || !k || !v || N < 1 || d < 1 || prefix_len < 0 || prefix_len > N || isnan(tau) ||
         (mode != ORACLE_DENSE && mode != ORACLE_SPARSE && mode != ORACLE_TOPK))
         return -1;
+    if (flags & ~(ORACLE_PREFIX_ROWS | ORACLE_VIDEO_STATS)) return -1;
+    if ((flags & ORACLE_PREFIX_ROWS) && mode == ORACLE_DENSE) return -1;
+    if ((flags & ORACLE_VIDEO_STATS) && mode != ORACLE_SPARSE) return -1;
     if (mode == ORACLE_TOPK && !(tau > 0.0 && tau <= 1.0)) return -1;
     int64_t Nb = (N + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
     int64_t Pb = (prefix_len + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
@@ -240,11 +265,13 @@ int solattn_oracle_head(const double* q, const double* k, const double* v,
             for (int64_t j = 0; j < Nb; ++j) keep[j] = mask_override[i * Nb + j] ? 1 : 0;
         } else if (mode == ORACLE_DENSE) {
             for (int64_t j = 0; j < Nb; ++j) keep[j] = 1;
-        } else if (mode == ORACLE_TOPK) {
-            thr = kth_largest(s, Pb, Nb, topk_count(tau, Pb, Nb), sorted);
-            for (int64_t j = 0; j < Nb; ++j) keep[j] = (j < Pb) || (s[j] >= thr);
         } else {
-            thr = row_threshold(s, Nb, tau);
+            if ((flags & ORACLE_PREFIX_ROWS) && i < Pb)
+                thr = -INFINITY;  /* a prefix query block keeps every key block */
+            else if (mode == ORACLE_TOPK)
+                thr = kth_largest(s, Pb, Nb, topk_count(tau, Pb, Nb), sorted);
+            else
+                thr = row_threshold(s, (flags & ORACLE_VIDEO_STATS) ? Pb : 0, Nb, tau);
             for (int64_t j = 0; j < Nb; ++j) keep[j] = (j < Pb) || (s[j] >= thr);
         }
         if (mask_out) memcpy(mask_out + i * Nb, keep, Nb);

@@ -101,7 +101,8 @@ def test_threshold_worked_examples():
     for c in cases:
         tau = float(c["tau"])
         q, k, v = _score_row_inputs(c["scores"])
-        r = oracle.head(q, k, v, 64 * c["prefix_blocks"], tau, want_out=False)
+        mode = oracle.SPARSE | (oracle.VIDEO_STATS if c.get("video_stats") else 0)
+        r = oracle.head(q, k, v, 64 * c["prefix_blocks"], tau, mode=mode, want_out=False)
         assert np.allclose(r["score"][0], c["scores"], atol=1e-15)
         thr = float(c["thr"])
         if math.isinf(thr):
@@ -109,6 +110,53 @@ def test_threshold_worked_examples():
         else:
             assert abs(r["thr"][0] - thr) < 1e-12, c
         assert list(r["mask"][0]) == c["keep"], c
+
+
+@pytest.mark.parametrize("base", [oracle.SPARSE, oracle.TOPK])
+def test_prefix_rows_variant_keeps_every_block(base):
+    # PREFIX_ROWS: query blocks inside the prefix keep every key block (their
+    # rows are plain dense attention); the other rows route as without it
+    rng = np.random.default_rng(41)
+    N, d, prefix = 64 * 12 + 20, 32, 150   # Pb = 3, ragged last block
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    tau = math.inf if base == oracle.SPARSE else 0.25
+    plain = oracle.head(q, k, v, prefix, tau, mode=base)
+    var = oracle.head(q, k, v, prefix, tau, mode=base | oracle.PREFIX_ROWS)
+    dense = oracle.head(q, k, v, prefix, 0.0, mode=oracle.DENSE)
+    pb = 3
+    assert var["mask"][:pb].all()
+    assert np.all(var["thr"][:pb] == -math.inf)
+    assert np.array_equal(var["mask"][pb:], plain["mask"][pb:])
+    assert np.array_equal(var["thr"][pb:], plain["thr"][pb:])
+    if base == oracle.SPARSE:
+        assert not plain["mask"][:pb, pb:].any()   # tau = +inf: prefix only
+    rows = slice(0, 64 * pb)
+    assert np.array_equal(var["out"][rows], dense["out"][rows])
+    assert np.array_equal(var["out"][64 * pb:], plain["out"][64 * pb:])
+
+
+def test_video_stats_variant_on_random_rows():
+    # VIDEO_STATS: the threshold of every row is mean + tau * population std
+    # of its video scores, recomputed here with numpy from the oracle's scores
+    rng = np.random.default_rng(42)
+    N, d, prefix = 64 * 20, 32, 200   # Pb = 4
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    r = oracle.head(q, k, v, prefix, 0.8, mode=oracle.SPARSE | oracle.VIDEO_STATS, want_out=False)
+    video = r["score"][:, 4:]
+    thr = video.mean(1) + 0.8 * video.std(1)
+    assert np.allclose(r["thr"], thr, rtol=0, atol=1e-12)
+    keep = np.concatenate([np.ones((20, 4), bool), r["score"][:, 4:] >= r["thr"][:, None]], 1)
+    assert np.array_equal(r["mask"].astype(bool), keep)
+    whole = oracle.head(q, k, v, prefix, 0.8, want_out=False)
+    assert not np.allclose(whole["thr"], r["thr"])
+
+
+def test_variant_flags_rejected_where_they_do_not_apply():
+    q = k = v = np.zeros((128, 8))
+    for mode, tau in ((oracle.DENSE | oracle.PREFIX_ROWS, 0.0), (oracle.TOPK | oracle.VIDEO_STATS, 0.5),
+                      (oracle.DENSE | oracle.VIDEO_STATS, 0.0), (oracle.SPARSE | 0x40, 1.0)):
+        with pytest.raises(ValueError):
+            oracle.head(q, k, v, 64, tau, mode=mode)
 
 
 @pytest.mark.parametrize("tau", [-1.0, 0.0, 1.0, 2.5, math.inf])
