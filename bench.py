@@ -372,6 +372,22 @@ def main():
             sweep[str(t)] = {"ms": round(tms, 4), "video_sparsity": round(float(1 - m[..., pb:].mean()), 4),
                              "speedup_vs_dense": round(dms / tms, 2)}
         res["tau_sweep"] = sweep
+        # routing variants (mode flags) at the headline tau
+        variants = {}
+        for vm in ("sparse+video_stats", "sparse+prefix_rows"):
+            def vf(vm=vm):
+                sa.solattn_forward_ws(qd, kd, vd, out, w.prefix_len, tau, vm, ws)
+            vf()
+            vms = float(np.median(time_calls(vf, 20, stream)))
+            # (the routing-only call takes no variant flags: the mask comes
+            # from the debug forward)
+            _, wv, _, _ = sa.solattn_forward_debug(qd, kd, vd, None, w.prefix_len, tau, vm,
+                                                   want_scores=False)
+            torch.cuda.synchronize()
+            mv = sa.unpack_mask(wv, w.nb)
+            variants[vm] = {"ms": round(vms, 4), "speedup_vs_dense": round(dms / vms, 2),
+                            "video_sparsity": round(float(1 - mv[..., pb:].mean()), 4)}
+        res["routing_variants"] = variants
         # routing setup (pooling + scoring/threshold, no attention)
         mw = torch.zeros((B, H, w.nb, (w.nb + 31) // 32), dtype=torch.int32, device="cuda")
         th = torch.zeros((B, H, w.nb), dtype=torch.float32, device="cuda")

@@ -85,7 +85,9 @@ struct AttnArgs {
     int64_t Pb;
     float tau;
     int64_t topk;         // kTopk: video key blocks kept per query block
-    int d, dtype, mode;
+    int d, dtype, mode;   // mode: kDense, kSparse or kTopk (the flags below apart)
+    int prefix_rows;      // query blocks i < Pb keep every key block
+    int video_stats;      // kSparse: threshold statistics over key blocks j >= Pb
 };
 
 hipError_t launch_pool(const PoolArgs& a, int64_t BH, hipStream_t s);

@@ -11,6 +11,11 @@
 // product scaled by 1/sqrt(d); the standard deviation is the population one
 // over all Nb key blocks; a score equal to the threshold is kept; tau = -inf
 // keeps all, tau = +inf keeps only the prefix, sigma = 0 uses the mean.
+// Two variants take the other reading of a passage: prefix_rows (query
+// blocks of the prefix keep every key block: the packed prefix's exact
+// attention read on the query side too, page "英伟达开源 Sol-H3", section 2.2)
+// and video_stats (mean and standard deviation over the video key blocks
+// only; +inf when there is none).
 //
 // In the fixed-ratio mode the threshold is instead the k-th largest video
 // score of the row (kth_largest_video) and skipped blocks get no pooled term.
@@ -115,25 +120,31 @@ __device__ inline RouteResult route_select(const AttnArgs& a, int64_t bh, int64_
     const int lane = threadIdx.x & 63;
     const int64_t Nb = a.Nb, Nbp = a.Nbp;
     float thr;
-    if (a.mode == kTopk) {
+    if (a.prefix_rows && i < a.Pb) {
+        thr = -__builtin_inff();  // a prefix query block keeps every key block
+    } else if (a.mode == kTopk) {
         thr = kth_largest_video(srow, a.Pb, Nb, a.topk);
+    } else if (__builtin_isinf(a.tau)) {
+        thr = a.tau;
     } else {
-        // row statistics, two passes (mean, then squared deviations)
-        float part = 0.f;
-        for (int64_t j = lane; j < Nb; j += 64) part += srow[j];
-        const float mu = wave_sum(part) / (float)Nb;
-        part = 0.f;
-        for (int64_t j = lane; j < Nb; j += 64) {
-            const float t = srow[j] - mu;
-            part += t * t;
+        // row statistics, two passes (mean, then squared deviations), over the
+        // whole row or, with video_stats, over the video blocks [Pb, Nb)
+        const int64_t lo = a.video_stats ? a.Pb : 0;
+        if (lo >= Nb) {
+            thr = __builtin_inff();  // no video block: only the prefix is kept
+        } else {
+            const float n = (float)(Nb - lo);
+            float part = 0.f;
+            for (int64_t j = lo + lane; j < Nb; j += 64) part += srow[j];
+            const float mu = wave_sum(part) / n;
+            part = 0.f;
+            for (int64_t j = lo + lane; j < Nb; j += 64) {
+                const float t = srow[j] - mu;
+                part += t * t;
+            }
+            const float sigma = sqrtf(wave_sum(part) / n);
+            thr = sigma == 0.f ? mu : mu + a.tau * sigma;
         }
-        const float sigma = sqrtf(wave_sum(part) / (float)Nb);
-        if (__builtin_isinf(a.tau))
-            thr = a.tau;
-        else if (sigma == 0.f)
-            thr = mu;
-        else
-            thr = mu + a.tau * sigma;
     }
 
     // keep bits, kept list, pooled-tile flags, pooled biases (log2 n_j: 6

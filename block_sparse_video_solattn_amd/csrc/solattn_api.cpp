@@ -57,9 +57,16 @@ int validate(const void* q, const void* k, const void* v, const void* out, bool 
     if (prefix_len < 0 || prefix_len > N)
         return fail(SOLATTN_EINVAL, "prefix_len must lie in [0, N] (got %lld)", (long long)prefix_len);
     if (std::isnan(tau)) return fail(SOLATTN_EINVAL, "tau must not be NaN");
-    if (mode != SOLATTN_DENSE && mode != SOLATTN_SPARSE && mode != SOLATTN_TOPK)
+    const int base = mode & SOLATTN_MODE_MASK, flags = mode & ~SOLATTN_MODE_MASK;
+    if (base != SOLATTN_DENSE && base != SOLATTN_SPARSE && base != SOLATTN_TOPK)
         return fail(SOLATTN_EINVAL, "unknown mode %d", mode);
-    if (mode == SOLATTN_TOPK && need_out && !(tau > 0.f && tau <= 1.f))
+    if (flags & ~(SOLATTN_PREFIX_ROWS | SOLATTN_VIDEO_STATS))
+        return fail(SOLATTN_EINVAL, "unknown mode flags 0x%x", flags);
+    if ((flags & SOLATTN_PREFIX_ROWS) && base == SOLATTN_DENSE)
+        return fail(SOLATTN_EINVAL, "SOLATTN_PREFIX_ROWS needs SPARSE or TOPK");
+    if ((flags & SOLATTN_VIDEO_STATS) && base != SOLATTN_SPARSE)
+        return fail(SOLATTN_EINVAL, "SOLATTN_VIDEO_STATS needs SPARSE");
+    if (base == SOLATTN_TOPK && need_out && !(tau > 0.f && tau <= 1.f))
         return fail(SOLATTN_EINVAL, "topk mode: tau is the kept fraction, in (0, 1] (got %g)",
                     (double)tau);
     if (dtype != SOLATTN_F32 && dtype != SOLATTN_BF16)
@@ -140,7 +147,7 @@ int run_prepare(const void* q, const void* k, const void* v, int64_t B, int64_t 
     p.Nbp = (p.Nb + 63) / 64 * 64;
     p.d = (int)d;
     p.dtype = dtype;
-    p.pooled = mode != SOLATTN_DENSE;
+    p.pooled = (mode & SOLATTN_MODE_MASK) != SOLATTN_DENSE;
     p.pack = pack && dtype == kBF16;
     if (!p.pooled && !p.pack) return SOLATTN_OK;  // fp32 dense: nothing to prepare
     hipError_t e = launch_pool(p, B * H, s);
@@ -167,7 +174,8 @@ int run_attend(const void* q, const void* k, const void* v, void* out, int64_t B
     a.kbarT = reinterpret_cast<const float*>(at(ws, L.kbarT));
     a.out = out;
     a.mask_out = mask_out;
-    a.score_out = mode != SOLATTN_DENSE ? score_out : nullptr;
+    const int base = mode & SOLATTN_MODE_MASK;
+    a.score_out = base != SOLATTN_DENSE ? score_out : nullptr;
     a.thr_out = thr_out;
     a.BH = B * H;
     a.N = N;
@@ -177,12 +185,14 @@ int run_attend(const void* q, const void* k, const void* v, void* out, int64_t B
     a.tau = tau;
     a.d = (int)d;
     a.dtype = dtype;
-    a.mode = mode;
+    a.mode = base;
+    a.prefix_rows = (mode & SOLATTN_PREFIX_ROWS) != 0;
+    a.video_stats = (mode & SOLATTN_VIDEO_STATS) != 0;
     // topk: k = ceil(tau * video key blocks), evaluated in double on the host
     // so that every query block (and any reference) uses the same count
     {
         const int64_t nv = a.Nb - a.Pb;
-        int64_t kk = mode == SOLATTN_TOPK ? (int64_t)std::ceil((double)tau * (double)nv) : 0;
+        int64_t kk = base == SOLATTN_TOPK ? (int64_t)std::ceil((double)tau * (double)nv) : 0;
         a.topk = kk > nv ? nv : kk;
     }
     hipError_t e = route_only ? launch_route(a, s)

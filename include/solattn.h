@@ -77,6 +77,24 @@ extern "C" {
  */
 #define SOLATTN_TOPK 2
 
+/*
+ * Routing variants, OR-ed into mode (the base mode is mode & SOLATTN_MODE_MASK).
+ * Each takes the other reading of a passage the default routing reads one
+ * way; a flag outside the modes named here is SOLATTN_EINVAL.
+ *   SOLATTN_PREFIX_ROWS (SPARSE or TOPK): the packed prefix's exact attention
+ *     (page "英伟达开源 Sol-H3", section 2.2) read on the query side too:
+ *     query blocks i < ceil(prefix_len/64) keep every key block (their rows
+ *     are plain dense attention; threshold -inf in the debug export).
+ *   SOLATTN_VIDEO_STATS (SPARSE): the mean and standard deviation of the
+ *     threshold (page "MiniMax 官宣 NVIDIA Sol 团队 H3 加速:5 秒视频 1.653
+ *     秒生成并开源", section "提速来自流水线每一段的叠加") are taken over the
+ *     video key blocks j >= ceil(prefix_len/64) only; a row with no video
+ *     block has threshold +inf (only the prefix is kept).
+ */
+#define SOLATTN_MODE_MASK 0x0f
+#define SOLATTN_PREFIX_ROWS 0x10
+#define SOLATTN_VIDEO_STATS 0x20
+
 /* dtype */
 #define SOLATTN_F32 0
 #define SOLATTN_BF16 1

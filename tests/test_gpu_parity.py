@@ -26,7 +26,10 @@ def check_forward(q, k, v, dtype, prefix, tau, mode="sparse", rows_blocks=None):
     """GPU forward vs oracle recomputed with the GPU's mask; returns stats."""
     B, H, N, d = q.shape
     gout, gmask, gs, gthr = gpu_debug(q, k, v, dtype, prefix, tau, mode)
-    omode = {"sparse": oracle.SPARSE, "dense": oracle.DENSE, "topk": oracle.TOPK}[mode]
+    parts = mode.split("+")
+    omode = {"sparse": oracle.SPARSE, "dense": oracle.DENSE, "topk": oracle.TOPK}[parts[0]]
+    for f in parts[1:]:
+        omode |= {"prefix_rows": oracle.PREFIX_ROWS, "video_stats": oracle.VIDEO_STATS}[f]
     otau = float(np.float32(tau))  # the value the C ABI received
     n_diff = n_near = 0
     worst = 0.0
@@ -40,12 +43,13 @@ def check_forward(q, k, v, dtype, prefix, tau, mode="sparse", rows_blocks=None):
                 n_near += nn
                 fin = np.isfinite(ores["score"])
                 assert np.max(np.abs(gs[b, h][fin] - ores["score"][fin])) < 1e-4
-                if mode == "sparse" and math.isinf(tau):
-                    assert np.all(gthr[b, h] == tau)
-                else:
-                    fin_t = np.isfinite(ores["thr"])
-                    assert np.array_equal(np.isfinite(gthr[b, h]), fin_t)
-                    assert np.max(np.abs(gthr[b, h][fin_t] - ores["thr"][fin_t]), initial=0) < 1e-4
+                # the same infinite thresholds (tau = +-inf, rows with no video
+                # block, prefix rows of the PREFIX_ROWS variant), the finite
+                # ones within the score tolerance
+                fin_t = np.isfinite(ores["thr"])
+                assert np.array_equal(np.isfinite(gthr[b, h]), fin_t)
+                assert np.array_equal(gthr[b, h][~fin_t], ores["thr"][~fin_t])
+                assert np.max(np.abs(gthr[b, h][fin_t] - ores["thr"][fin_t]), initial=0) < 1e-4
             else:
                 assert gmask[b, h].all()
             r = oracle.head(q[b, h], k[b, h], v[b, h], prefix, otau, mode=omode,
@@ -244,6 +248,29 @@ def test_topk_fraction_one_matches_dense():
     b = sa.solattn_forward(qd, kd, vd, None, 64, 0.0, "dense")
     torch.cuda.synchronize()
     assert (a.float() - b.float()).abs().max().item() <= 1e-2
+
+
+# ------------------------------------------------------- routing variants
+@pytest.mark.parametrize("mode,tau", [("sparse+prefix_rows", 1.0), ("sparse+prefix_rows", math.inf),
+                                      ("sparse+video_stats", 1.25), ("topk+prefix_rows", 0.2),
+                                      ("sparse+prefix_rows+video_stats", 0.75)])
+@pytest.mark.parametrize("dtype,N,d", [("bf16", 64 * 20 + 17, 128), ("f32", 64 * 12 + 40, 64)])
+def test_routing_variants(mode, tau, dtype, N, d):
+    prefix = 150  # 3 prefix blocks, the third one partly prefix
+    q, k, v = inputs.custom(1, 2, N, d, dtype, prefix_len=prefix, seed=71, kind="field",
+                            grid=(2, 12, 50))
+    st = check_forward(q, k, v, dtype, prefix, tau, mode)
+    pb = 3
+    assert st["mask"][..., :pb].all()
+    if "prefix_rows" in mode:
+        assert st["mask"][..., :pb, :].all()
+
+
+def test_video_stats_without_video_blocks():
+    # the whole sequence is prefix: every row keeps every block, thresholds +inf
+    q, k, v = inputs.custom(1, 1, 700, 64, "bf16", prefix_len=700, seed=72)
+    st = check_forward(q, k, v, "bf16", 700, 1.0, "sparse+video_stats")
+    assert st["mask"].all()
 
 
 def test_pooled_only_path_f32():
