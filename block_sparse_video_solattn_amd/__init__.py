@@ -12,6 +12,8 @@ _BINDING_NAMES = (
     "solattn_pool", "solattn_prepare_ws", "solattn_probe_mfma_bf16", "solattn_route",
     "solattn_strerror",
     "solattn_version", "solattn_workspace_bytes", "unpack_mask", "raw_call",
+    "solattn_transport_record_bytes", "solattn_pack_qkv_int8", "solattn_unpack_qkv_int8",
+    "solattn_pack_out_fp8", "solattn_unpack_out_fp8",
 )
 
 

@@ -51,6 +51,11 @@ _SIGS = {
     "solattn_pool": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P], _I),
     "solattn_route": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _P, _P, _P, _P], _I),
     "solattn_probe_mfma_bf16": ([_P, _I64, _I64, _P], _I),
+    "solattn_transport_record_bytes": ([_I64], _SZ),
+    "solattn_pack_qkv_int8": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P], _I),
+    "solattn_unpack_qkv_int8": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I),
+    "solattn_pack_out_fp8": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _P], _I),
+    "solattn_unpack_out_fp8": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _P], _I),
     "solattn_strerror": ([_I], ctypes.c_char_p),
     "solattn_last_error": ([], ctypes.c_char_p),
     "solattn_version": ([], ctypes.c_char_p),
@@ -257,3 +262,68 @@ def unpack_mask(words, nb: int):
 
 def isinf_tau(tau: float) -> bool:
     return math.isinf(tau)
+
+
+# ------------------------------------------------------- sequence-parallel transport
+def solattn_transport_record_bytes(d: int) -> int:
+    return int(_lib.solattn_transport_record_bytes(int(d)))
+
+
+def _bf16_4d(t, name):
+    import torch
+    if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous 4-d bfloat16 tensor" % name)
+    return tuple(t.shape)
+
+
+def solattn_pack_qkv_int8(q, k, v, P: int, send=None, stream=None):
+    """This rank's sequence shard q, k, v [B][H][Ns][d] -> INT8 records
+    [P][B][H/P][Ns][3][rec] (uint8), chunk p for rank p."""
+    import torch
+    B, H, Ns, d = _bf16_4d(q, "q")
+    if _bf16_4d(k, "k") != (B, H, Ns, d) or _bf16_4d(v, "v") != (B, H, Ns, d):
+        raise ValueError("q, k, v shapes differ")
+    rec = solattn_transport_record_bytes(d)
+    if send is None:
+        send = torch.empty((P, B, H // max(P, 1), Ns, 3, rec), dtype=torch.uint8, device=q.device)
+    _check(_lib.solattn_pack_qkv_int8(_ptr(q), _ptr(k), _ptr(v), B, H, Ns, d, int(P), _ptr(send),
+                                      _stream(stream)))
+    return send
+
+
+def solattn_unpack_qkv_int8(recv, d: int, q=None, k=None, v=None, stream=None):
+    """Received records [P][B][Hp][Ns][3][rec] -> q, k, v [B][Hp][P*Ns][d] bf16."""
+    import torch
+    P, B, Hp, Ns = (int(x) for x in recv.shape[:4])
+    shape = (B, Hp, P * Ns, d)
+    q = torch.empty(shape, dtype=torch.bfloat16, device=recv.device) if q is None else q
+    k = torch.empty(shape, dtype=torch.bfloat16, device=recv.device) if k is None else k
+    v = torch.empty(shape, dtype=torch.bfloat16, device=recv.device) if v is None else v
+    _check(_lib.solattn_unpack_qkv_int8(_ptr(recv), B, Hp, Ns, int(d), P, _ptr(q), _ptr(k), _ptr(v),
+                                        _stream(stream)))
+    return q, k, v
+
+
+def solattn_pack_out_fp8(o, P: int, send=None, stream=None):
+    """Output of this rank's heads o [B][Hp][P*Ns][d] -> FP8 records
+    [P][B][Hp][Ns][rec] (uint8), chunk r for rank r."""
+    import torch
+    B, Hp, N, d = _bf16_4d(o, "o")
+    if N % P:
+        raise ValueError("the sequence length must be a multiple of P")
+    Ns = N // P
+    if send is None:
+        send = torch.empty((P, B, Hp, Ns, solattn_transport_record_bytes(d)), dtype=torch.uint8,
+                           device=o.device)
+    _check(_lib.solattn_pack_out_fp8(_ptr(o), B, Hp, Ns, d, int(P), _ptr(send), _stream(stream)))
+    return send
+
+
+def solattn_unpack_out_fp8(recv, d: int, o=None, stream=None):
+    """Received records [P][B][Hp][Ns][rec] -> o [B][P*Hp][Ns][d] bf16."""
+    import torch
+    P, B, Hp, Ns = (int(x) for x in recv.shape[:4])
+    if o is None:
+        o = torch.empty((B, P * Hp, Ns, d), dtype=torch.bfloat16, device=recv.device)
+    _check(_lib.solattn_unpack_out_fp8(_ptr(recv), B, Hp, Ns, int(d), P, _ptr(o), _stream(stream)))
+    return o

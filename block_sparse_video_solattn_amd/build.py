@@ -11,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsolattn.so")
-SOURCES = ["solattn_api.cpp", "pool.hip", "route.hip", "attn_bf16.hip", "attn_f32.hip", "probe.hip"]
+SOURCES = ["solattn_api.cpp", "pool.hip", "route.hip", "attn_bf16.hip", "attn_f32.hip", "probe.hip",
+           "transport.hip"]
 ARCH = "gfx950"
 
 

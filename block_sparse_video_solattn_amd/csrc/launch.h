@@ -90,6 +90,37 @@ struct AttnArgs {
     int video_stats;      // kSparse: threshold statistics over key blocks j >= Pb
 };
 
+// Sequence-parallel transport (transport.hip); record = d codes + fp32 scale,
+// padded to a multiple of 16 bytes.
+struct QkvPackArgs {        // q, k, v [B][H][Ns][d] bf16 -> send [P][B][Hp][Ns][3][rec]
+    const void* q;
+    const void* k;
+    const void* v;
+    uint8_t* send;
+    int64_t B, H, Hp, Ns, P;
+};
+struct QkvUnpackArgs {      // recv [P][B][Hp][Ns][3][rec] -> q, k, v [B][Hp][P*Ns][d] bf16
+    const uint8_t* recv;
+    void* q;
+    void* k;
+    void* v;
+    int64_t B, Hp, Ns, P;
+};
+struct OutPackArgs {        // o [B][Hp][P*Ns][d] bf16 -> send [P][B][Hp][Ns][rec]
+    const void* o;
+    uint8_t* send;
+    int64_t B, Hp, Ns, P;
+};
+struct OutUnpackArgs {      // recv [P][B][Hp][Ns][rec] -> o [B][P*Hp][Ns][d] bf16
+    const uint8_t* recv;
+    void* o;
+    int64_t B, Hp, Ns, P;
+};
+hipError_t launch_pack_qkv_int8(const QkvPackArgs& a, int d, hipStream_t s);
+hipError_t launch_unpack_qkv_int8(const QkvUnpackArgs& a, int d, hipStream_t s);
+hipError_t launch_pack_out_fp8(const OutPackArgs& a, int d, hipStream_t s);
+hipError_t launch_unpack_out_fp8(const OutUnpackArgs& a, int d, hipStream_t s);
+
 hipError_t launch_pool(const PoolArgs& a, int64_t BH, hipStream_t s);
 hipError_t launch_route(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);

@@ -6,12 +6,14 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/solattn.h"
 #include "../../include/solattn_probe.h"
+#include "../../include/solattn_transport.h"
 #include "launch.h"
 
 using namespace solattn;
@@ -83,6 +85,41 @@ int validate(const void* q, const void* k, const void* v, const void* out, bool 
         if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
             overlaps(out, bytes, v, bytes))
             return fail(SOLATTN_EINVAL, "out must not overlap q, k or v");
+    }
+    return SOLATTN_OK;
+}
+
+// Transport calls: shapes (each factor >= 1, d 64 or 128, every launch's
+// rows well inside the grid limits).
+int check_transport(int64_t B, int64_t H, int64_t Ns, int64_t d, int64_t P) {
+    if (B < 1 || H < 1 || Ns < 1 || P < 1)
+        return fail(SOLATTN_EINVAL, "B, H, Ns, P must be >= 1 (got %lld, %lld, %lld, %lld)",
+                    (long long)B, (long long)H, (long long)Ns, (long long)P);
+    if (d != 64 && d != 128) return fail(SOLATTN_EINVAL, "d must be 64 or 128 (got %lld)", (long long)d);
+    const int64_t lim = int64_t(1) << 34;
+    if (B > lim / H || B * H > lim / Ns || B * H * Ns > lim / (3 * P))
+        return fail(SOLATTN_EUNSUPPORTED, "B*H*Ns*P too large");
+    return SOLATTN_OK;
+}
+
+// Transport calls: non-NULL, 16-byte aligned buffers, outputs not
+// overlapping inputs.
+int check_buffers(std::initializer_list<const void*> in, size_t in_bytes,
+                  std::initializer_list<const void*> out, size_t out_bytes) {
+    for (const void* p : in)
+        if (!p || !aligned16(p)) return fail(SOLATTN_EINVAL, "input buffers must be non-NULL and 16-byte aligned");
+    for (const void* p : out)
+        if (!p || !aligned16(p)) return fail(SOLATTN_EINVAL, "output buffers must be non-NULL and 16-byte aligned");
+    size_t a = 0;
+    for (const void* o : out) {
+        for (const void* i : in)
+            if (overlaps(o, out_bytes, i, in_bytes))
+                return fail(SOLATTN_EINVAL, "output buffers must not overlap the inputs");
+        size_t b = 0;
+        for (const void* o2 : out)
+            if (b++ > a && overlaps(o, out_bytes, o2, out_bytes))
+                return fail(SOLATTN_EINVAL, "output buffers must not overlap each other");
+        ++a;
     }
     return SOLATTN_OK;
 }
@@ -333,6 +370,64 @@ int solattn_probe_mfma_bf16(float* sink, int64_t waves, int64_t iters, void* str
     const hipError_t e = launch_probe_mfma(sink, waves, iters, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "probe launch");
     return SOLATTN_OK;
+}
+
+size_t solattn_transport_record_bytes(int64_t d) {
+    return (d == 64 || d == 128) ? (size_t)((d + 4 + 15) / 16 * 16) : 0;
+}
+
+int solattn_pack_qkv_int8(const void* q, const void* k, const void* v, int64_t B, int64_t H,
+                          int64_t Ns, int64_t d, int64_t P, void* send, void* stream) {
+    g_last_error.clear();
+    int rc = check_transport(B, H, Ns, d, P);
+    if (rc) return rc;
+    if (H % P) return fail(SOLATTN_EINVAL, "H (%lld) must be a multiple of P (%lld)", (long long)H,
+                           (long long)P);
+    const size_t tb = (size_t)B * H * Ns * d * 2, sb = (size_t)B * H * Ns * 3 *
+                                                         solattn_transport_record_bytes(d);
+    if ((rc = check_buffers({q, k, v}, tb, {send}, sb))) return rc;
+    QkvPackArgs a{q, k, v, static_cast<uint8_t*>(send), B, H, H / P, Ns, P};
+    const hipError_t e = launch_pack_qkv_int8(a, (int)d, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOLATTN_OK : hip_fail(e, "pack kernel launch");
+}
+
+int solattn_unpack_qkv_int8(const void* recv, int64_t B, int64_t Hp, int64_t Ns, int64_t d,
+                            int64_t P, void* q, void* k, void* v, void* stream) {
+    g_last_error.clear();
+    int rc = check_transport(B, Hp, Ns, d, P);
+    if (rc) return rc;
+    const size_t rb = (size_t)P * B * Hp * Ns * 3 * solattn_transport_record_bytes(d),
+                 tb = (size_t)B * Hp * P * Ns * d * 2;
+    if ((rc = check_buffers({recv}, rb, {q, k, v}, tb))) return rc;
+    QkvUnpackArgs a{static_cast<const uint8_t*>(recv), q, k, v, B, Hp, Ns, P};
+    const hipError_t e = launch_unpack_qkv_int8(a, (int)d, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOLATTN_OK : hip_fail(e, "unpack kernel launch");
+}
+
+int solattn_pack_out_fp8(const void* o, int64_t B, int64_t Hp, int64_t Ns, int64_t d, int64_t P,
+                         void* send, void* stream) {
+    g_last_error.clear();
+    int rc = check_transport(B, Hp, Ns, d, P);
+    if (rc) return rc;
+    const size_t tb = (size_t)B * Hp * P * Ns * d * 2,
+                 sb = (size_t)P * B * Hp * Ns * solattn_transport_record_bytes(d);
+    if ((rc = check_buffers({o}, tb, {send}, sb))) return rc;
+    OutPackArgs a{o, static_cast<uint8_t*>(send), B, Hp, Ns, P};
+    const hipError_t e = launch_pack_out_fp8(a, (int)d, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOLATTN_OK : hip_fail(e, "pack kernel launch");
+}
+
+int solattn_unpack_out_fp8(const void* recv, int64_t B, int64_t Hp, int64_t Ns, int64_t d,
+                           int64_t P, void* o, void* stream) {
+    g_last_error.clear();
+    int rc = check_transport(B, Hp, Ns, d, P);
+    if (rc) return rc;
+    const size_t rb = (size_t)P * B * Hp * Ns * solattn_transport_record_bytes(d),
+                 tb = (size_t)B * P * Hp * Ns * d * 2;
+    if ((rc = check_buffers({recv}, rb, {o}, tb))) return rc;
+    OutUnpackArgs a{static_cast<const uint8_t*>(recv), o, B, Hp, Ns, P};
+    const hipError_t e = launch_unpack_out_fp8(a, (int)d, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOLATTN_OK : hip_fail(e, "unpack kernel launch");
 }
 
 const char* solattn_version(void) { return "solattn-mi355x 0.1.0 (gfx950)"; }

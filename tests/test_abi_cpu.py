@@ -117,3 +117,30 @@ def test_probe_rejects_bad_arguments_on_host(lib):
     assert probe(A, (1 << 20) + 1, 16) == lib.EINVAL
     assert probe(A, 1024, 0) == lib.EINVAL
     assert "iters" in lib.solattn_last_error()
+
+
+def test_transport_record_bytes(lib):
+    assert lib.solattn_transport_record_bytes(128) == 144
+    assert lib.solattn_transport_record_bytes(64) == 80
+    assert lib.solattn_transport_record_bytes(96) == 0
+
+
+def test_transport_entry_points_validate(lib):
+    # every rejection happens on the host, before any device call
+    X, Y, Z, S = A, A + 0x1000000, A + 0x2000000, A + 0x3000000
+    pack = lambda q=X, k=Y, v=Z, B=1, H=4, Ns=64, d=128, P=2, send=S: lib.raw_call(
+        "solattn_pack_qkv_int8", q, k, v, B, H, Ns, d, P, send, None)
+    assert pack(q=None) == 1
+    assert pack(send=S + 8) == 1
+    assert pack(d=96) == 1
+    assert pack(P=0) == 1
+    assert pack(H=6, P=4) == 1
+    assert pack(send=X + 0x100) == 1          # output overlaps q
+    assert pack(B=1 << 40) == 2
+    unpack = lambda B=1, Hp=2, Ns=64, d=128, P=2, q=X, k=Y, v=Z: lib.raw_call(
+        "solattn_unpack_qkv_int8", S, B, Hp, Ns, d, P, q, k, v, None)
+    assert unpack(k=X) == 1                   # two outputs overlap
+    assert unpack(Hp=0) == 1
+    assert lib.raw_call("solattn_pack_out_fp8", X, 1, 2, 64, 64, 2, None, None) == 1
+    assert lib.raw_call("solattn_unpack_out_fp8", S, 1, 2, 64, 32, 2, X, None) == 1
+    assert lib.solattn_last_error() != ""

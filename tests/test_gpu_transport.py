@@ -1,0 +1,136 @@
+"""GPU parity of the sequence-parallel transport kernels against the oracle
+(oracle/transport.py): INT8 and FP8 codes, scales and padding bit for bit,
+unpacked bf16 values bit for bit, and a whole exchange among P emulated ranks
+on one GPU (the all-to-all itself is a chunk copy here)."""
+import numpy as np
+import pytest
+
+from oracle import transport as T
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def bf16_values(rng, shape):
+    """float32 arrays of bf16-representable values with row scales spread
+    over several decades, a zero row and quantization ties."""
+    x = rng.standard_normal(shape) * np.exp(rng.uniform(-6, 6, shape[:-1] + (1,)))
+    x = T.to_bf16(x.astype(np.float32))
+    flat = x.reshape(-1, shape[-1])
+    flat[0] = 0.0                                        # zero row: scale 0
+    flat[1] = 0.0
+    flat[1, :4] = [127.0, 63.5, -0.5, 1.5]               # INT8 ties to even (inv = 1)
+    if flat.shape[0] > 2:
+        flat[2] = 0.0
+        flat[2, :5] = [448.0, 1.0625, 1.1875, 1.5 * 2 ** -9, -0.5 * 2 ** -9]  # E4M3 ties (inv = 1)
+    return x
+
+
+def to_dev(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(torch.bfloat16).contiguous()
+
+
+def to_np_bf16(t):
+    import torch
+    return t.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("P,B,H,Ns,d", [(2, 1, 4, 37, 128), (4, 2, 8, 5, 64), (1, 1, 3, 130, 128)])
+def test_pack_qkv_int8_bit_exact(P, B, H, Ns, d):
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    rng = np.random.default_rng(11)
+    q, k, v = (bf16_values(rng, (B, H, Ns, d)) for _ in range(3))
+    send = sa.solattn_pack_qkv_int8(to_dev(q), to_dev(k), to_dev(v), P)
+    torch.cuda.synchronize()
+    ref = T.pack_qkv_int8(q, k, v, P)
+    got = send.cpu().numpy()
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("P,B,Hp,Ns,d", [(2, 1, 2, 37, 128), (3, 2, 1, 7, 64)])
+def test_unpack_qkv_int8_bit_exact(P, B, Hp, Ns, d):
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    rng = np.random.default_rng(12)
+    # receive buffer as P ranks' pack calls would leave it (oracle-made)
+    shards = [[bf16_values(rng, (B, Hp * P, Ns, d)) for _ in range(3)] for _ in range(P)]
+    recv = T.all_to_all([T.pack_qkv_int8(*sh, P) for sh in shards])[0]
+    got = sa.solattn_unpack_qkv_int8(torch.from_numpy(recv).cuda(), d)
+    torch.cuda.synchronize()
+    ref = T.unpack_qkv_int8(recv, d)
+    for g, r in zip(got, ref):
+        assert np.array_equal(to_np_bf16(g).view(np.uint32), r.view(np.uint32))
+
+
+@pytest.mark.parametrize("P,B,Hp,Ns,d", [(2, 1, 2, 37, 128), (4, 1, 3, 5, 64), (1, 2, 1, 130, 128)])
+def test_pack_out_fp8_bit_exact(P, B, Hp, Ns, d):
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    rng = np.random.default_rng(13)
+    o = bf16_values(rng, (B, Hp, P * Ns, d))
+    send = sa.solattn_pack_out_fp8(to_dev(o), P)
+    torch.cuda.synchronize()
+    ref = T.pack_out_fp8(o, P)
+    got = send.cpu().numpy()
+    assert got.shape == ref.shape
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, (bad[:5], got[tuple(bad[0])], ref[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("P,B,Hp,Ns,d", [(2, 1, 2, 37, 128), (3, 1, 1, 7, 64)])
+def test_unpack_out_fp8_bit_exact(P, B, Hp, Ns, d):
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    rng = np.random.default_rng(14)
+    outs = [bf16_values(rng, (B, Hp, P * Ns, d)) for _ in range(P)]
+    recv = T.all_to_all([T.pack_out_fp8(o, P) for o in outs])[1 % P]
+    got = sa.solattn_unpack_out_fp8(torch.from_numpy(recv).cuda(), d)
+    torch.cuda.synchronize()
+    ref = T.unpack_out_fp8(recv, d)
+    assert np.array_equal(to_np_bf16(got).view(np.uint32), ref.view(np.uint32))
+
+
+def test_exchange_round_trip_on_one_gpu():
+    # P ranks emulated on one GPU: pack per destination, exchange the chunks,
+    # unpack; then the output back the same way.  Every value must equal the
+    # oracle's, and the round trip stays within the quantization error.
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    P, B, H, Ns, d = 4, 1, 8, 48, 128
+    Hp = H // P
+    rng = np.random.default_rng(15)
+    full = [bf16_values(rng, (B, H, P * Ns, d)) for _ in range(3)]
+    sends = [sa.solattn_pack_qkv_int8(*(to_dev(x[:, :, s * Ns:(s + 1) * Ns]) for x in full), P)
+             for s in range(P)]
+    recvs = [torch.stack([sends[s][p] for s in range(P)]).contiguous() for p in range(P)]
+    got = [sa.solattn_unpack_qkv_int8(recvs[p], d) for p in range(P)]
+    torch.cuda.synchronize()
+    ref = T.all_to_all([T.pack_qkv_int8(*(x[:, :, s * Ns:(s + 1) * Ns] for x in full), P)
+                        for s in range(P)])
+    for p in range(P):
+        rq = T.unpack_qkv_int8(ref[p], d)
+        for g, r, x in zip(got[p], rq, full):
+            gv = to_np_bf16(g)
+            assert np.array_equal(gv, r)
+            xs = x[:, p * Hp:(p + 1) * Hp]
+            amax = np.abs(xs).max(-1, keepdims=True)
+            assert np.all(np.abs(gv - xs) <= amax / 127 * 0.5 * 1.001 + np.abs(gv) * 2.0 ** -8)
+    # output: rank p holds heads p*Hp.. over the full sequence
+    o_heads = [to_dev(bf16_values(rng, (B, Hp, P * Ns, d))) for _ in range(P)]
+    osend = [sa.solattn_pack_out_fp8(o, P) for o in o_heads]
+    orecv = [torch.stack([osend[s][r] for s in range(P)]).contiguous() for r in range(P)]
+    oback = [sa.solattn_unpack_out_fp8(orecv[r], d) for r in range(P)]
+    torch.cuda.synchronize()
+    for r in range(P):
+        for p in range(P):
+            ref_rows = T.dequant_fp8(*T.quant_fp8(to_np_bf16(o_heads[p])[:, :, r * Ns:(r + 1) * Ns]))
+            assert np.array_equal(to_np_bf16(oback[r])[:, p * Hp:(p + 1) * Hp], ref_rows)
