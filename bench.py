@@ -219,6 +219,75 @@ def long_clip_check(sa, stream):
             "attn_kept_mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
 
 
+def sp_rank_check(sa, stream, q_all, k_all, v_all, prefix_len, tau, P=8):
+    """One rank's share of a P-GPU sequence-parallel step on the refine
+    shape (heads 0 .. H/P - 1 over the whole sequence), with the transport
+    kernels around the attention: pack this rank's sequence shard of every
+    head (INT8), unpack the received records, attend, pack the output (FP8),
+    unpack the received output.  The all-to-all itself needs P GPUs and is
+    left out; its chunks are copied here.  Also reports what the INT8 / FP8
+    round trip changes: routing bits and output difference against the
+    bf16 path on the same heads."""
+    import numpy as np
+    import torch
+    B, H, N, d = (int(x) for x in q_all.shape)
+    Hp, Ns = H // P, N // P
+    rec = sa.solattn_transport_record_bytes(d)
+    shards = [[x[:, :, s * Ns:(s + 1) * Ns].contiguous() for x in (q_all, k_all, v_all)]
+              for s in range(P)]
+    sends = [sa.solattn_pack_qkv_int8(*sh, P) for sh in shards]
+    recv = torch.stack([sends[s][0] for s in range(P)]).contiguous()   # rank 0's receive buffer
+    del sends
+    q8, k8, v8 = sa.solattn_unpack_qkv_int8(recv, d)
+    out8 = torch.empty_like(q8)
+    ws = torch.empty(sa.solattn_workspace_bytes(B, Hp, N, d, sa.BF16), dtype=torch.uint8,
+                     device="cuda")
+    t = {}
+    send_buf = torch.empty((P, B, H // P, Ns, 3, rec), dtype=torch.uint8, device="cuda")
+    t["pack_qkv_int8"] = lambda: sa.solattn_pack_qkv_int8(*shards[0], P, send=send_buf)
+    t["unpack_qkv_int8"] = lambda: sa.solattn_unpack_qkv_int8(recv, d, q8, k8, v8)
+    t["attention"] = lambda: sa.solattn_forward_ws(q8, k8, v8, out8, prefix_len, tau, "sparse", ws)
+    osend = torch.empty((P, B, Hp, Ns, rec), dtype=torch.uint8, device="cuda")
+    t["pack_out_fp8"] = lambda: sa.solattn_pack_out_fp8(out8, P, send=osend)
+    t["attention"]()
+    t["pack_out_fp8"]()
+    orecv = osend.clone()   # stands in for the chunks arriving from the P head groups
+    ob = torch.empty((B, P * Hp, Ns, d), dtype=torch.bfloat16, device="cuda")
+    t["unpack_out_fp8"] = lambda: sa.solattn_unpack_out_fp8(orecv, d, o=ob)
+    ms = {}
+    for name, fn in t.items():
+        fn()
+        ms[name] = float(np.median(time_calls(fn, 20, stream)))
+    nbytes = {"pack_qkv_int8": 3 * B * H * Ns * (2 * d + rec),
+              "unpack_qkv_int8": 3 * P * B * Hp * Ns * (rec + 2 * d),
+              "pack_out_fp8": B * Hp * N * (2 * d + rec),
+              "unpack_out_fp8": P * B * Hp * Ns * (rec + 2 * d)}
+    res = {"workload": "refine, rank 0 of %d: %d heads x %d tokens attended; shards of %d tokens"
+                       % (P, Hp, N, Ns), "P": P, "tau": tau}
+    for name, v in ms.items():
+        e = {"ms": round(v, 4)}
+        if name in nbytes:
+            e["GBps"] = round(nbytes[name] / (v * 1e-3) / 1e9, 1)
+        res[name] = e
+    res["rank_step_ms_without_all_to_all"] = round(sum(ms.values()), 4)
+    # what the INT8 / FP8 round trip changes on these heads
+    qb, kb, vb = (x[:, :Hp].contiguous() for x in (q_all, k_all, v_all))
+    ob16, wb, _, _ = sa.solattn_forward_debug(qb, kb, vb, None, prefix_len, tau, "sparse",
+                                              want_scores=False)
+    _, w8, _, _ = sa.solattn_forward_debug(q8, k8, v8, None, prefix_len, tau, "sparse",
+                                           want_scores=False)
+    torch.cuda.synchronize()
+    nb = (N + 63) // 64
+    mb, m8 = sa.unpack_mask(wb, nb), sa.unpack_mask(w8, nb)
+    res["int8_qkv_routing_bits_changed"] = round(float((mb != m8).mean()), 6)
+    res["int8_qkv_out_max_abs_diff"] = round(float((out8.float() - ob16.float()).abs().max()), 5)
+    # the FP8 output round trip, on this rank's own output rows (shard 0 of its heads)
+    orow = out8[:, :, :Ns].float()
+    back = sa.solattn_unpack_out_fp8(torch.stack([osend[0]] * P).contiguous(), d)[:, :Hp].float()
+    res["fp8_out_max_abs_diff"] = round(float((back - orow).abs().max()), 5)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -396,6 +465,7 @@ def main():
             sa.solattn_route(qd, kd, vd, w.prefix_len, tau, want_scores=False, mask=mw, thr=th)
         setup()
         res["setup_ms"] = round(float(np.median(time_calls(setup, 20, stream))), 4)
+        res["sp_rank_p8"] = sp_rank_check(sa, stream, qd, kd, vd, w.prefix_len, tau)
         del qd, kd, vd, out, ws, dev
         torch.cuda.empty_cache()
         res["sparsity_90_check"] = draft_check(sa, stream)
