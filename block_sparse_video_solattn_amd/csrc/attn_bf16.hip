@@ -355,27 +355,50 @@ __device__ __forceinline__ void pv_then_head(const bf16x8 (&vA)[D / 32][2], cons
             }
 }
 
-// O = acc / l rounded to bf16; lane holds query 32*nt + l32 and
-// d = 32*mt + 8*g + 4*half + r.
+// x + (x of lane ^ 32), the same bits in both lanes (v_permlane32_swap, no LDS)
+__device__ __forceinline__ float sum_across_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// O = acc / l rounded to bf16.  Lane holds query 32*nt + l32 and, for each
+// 8-column group g of a 32-column tile mt, columns 8g + 4*half .. +3.  One
+// v_permlane32_swap per dword trades half of each pair of groups between
+// the lane halves, so that a lane holds 8 whole columns of one group (half
+// 0: odd groups, half 1: even groups) and writes them with one 16-byte store.
 template <int D>
 __device__ __forceinline__ void store_rows(const f32x16 (&oacc)[D / 32][2], const float (&lsum)[2],
                                            bf16* op, int64_t i, int64_t N, int half, int l32) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-        const float l = lsum[nt] + __shfl_xor(lsum[nt], 32, 64);
-        const float inv = 1.0f / l;
+        const float inv = 1.0f / sum_across_halves(lsum[nt]);
         const int64_t row = i * 64 + 32 * nt + l32;
-        if (row < N) {
 #pragma unroll
-            for (int mt = 0; mt < D / 32; ++mt)
+        for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    bf16x4 o;
+            for (int pr = 0; pr < 2; ++pr) {
+                uint32_t w[2][2];  // [group 2pr, 2pr+1][dword]: 4 bf16 of this lane's half
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] = to_bf16(oacc[mt][nt][4 * g + r] * inv);
-                    *reinterpret_cast<bf16x4*>(op + row * D + 32 * mt + 8 * g + 4 * half) = o;
-                }
-        }
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int v = 4 * (2 * pr + q) + 2 * j;
+                        bf16x2 b;
+                        b[0] = to_bf16(oacc[mt][nt][v] * inv);
+                        b[1] = to_bf16(oacc[mt][nt][v + 1] * inv);
+                        w[q][j] = __builtin_bit_cast(uint32_t, b);
+                    }
+                uint4 out;
+                const auto s0 = __builtin_amdgcn_permlane32_swap(w[1][0], w[0][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(w[1][1], w[0][1], false, false);
+                out.x = s0[0];
+                out.y = s1[0];
+                out.z = s0[1];
+                out.w = s1[1];
+                if (row < N)
+                    *reinterpret_cast<uint4*>(op + row * D + 32 * mt + 16 * pr + 8 * (1 - half)) = out;
+            }
     }
 }
 
