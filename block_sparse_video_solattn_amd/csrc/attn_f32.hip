@@ -39,6 +39,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
         n_kept = (int)Nb;
         tile_mask = 0;
     }
+    __syncthreads();  // the routing's LDS lists are complete
 
     const float* qp = reinterpret_cast<const float*>(a.q) + bh * N * D;
     const float* kp = reinterpret_cast<const float*>(a.k) + bh * N * D;

@@ -111,7 +111,7 @@ __device__ inline void route_scores(const AttnArgs& a, int64_t bh, int64_t i, fl
     __syncthreads();
 }
 
-// route_select, from the scores in srow.  On return:
+// route_select, from the scores in srow (one wavefront).  On return:
 //   klist[0..n_kept)  kept key-block indices (ascending)
 //   srow[0..Nbp)      log2(n_j) for skipped blocks, -inf for kept and padding
 //                     (the per-column bias of the pooled tiles, log2 units)
@@ -175,7 +175,8 @@ __device__ inline RouteResult route_select(const AttnArgs& a, int64_t bh, int64_
         srow[j] = skip ? (j == nb - 1 ? log2_last : 6.0f) : -__builtin_inff();
     }
     if (a.thr_out && lane == 0) a.thr_out[bh * Nb + i] = thr;
-    __syncthreads();
+    // (no workgroup barrier here: the lists are this wave's own LDS; callers
+    // synchronise before other waves, or later code, read them)
     return RouteResult{n_kept, tile_mask};
 }
 

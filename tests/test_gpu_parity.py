@@ -306,11 +306,16 @@ def test_workspace_entry_points_match_forward():
     assert torch.equal(ref, out1) and torch.equal(ref, out2)
 
 
-def test_route_only_matches_debug_forward():
+@pytest.mark.parametrize("H,N,d,dtype", [(2, 3000, 128, "bf16"), (3, 64 * 9 + 5, 64, "f32"),
+                                         (1, 64 * 4096, 128, "bf16")])
+def test_route_only_matches_debug_forward(H, N, d, dtype):
+    # the routing-only kernel (four query blocks per workgroup; at N = 262144
+    # its LDS passes 64 KiB) gives the fused kernels' scores, thresholds and
+    # masks bit for bit, also for a last group of fewer than four blocks
     import torch
     import block_sparse_video_solattn_amd as sa
-    q, k, v = inputs.custom(1, 2, 3000, 128, "bf16", prefix_len=128, seed=36)
-    qd, kd, vd = device_tensors(q, k, v, "bf16")
+    q, k, v = inputs.custom(1, H, N, d, dtype, prefix_len=128, seed=36)
+    qd, kd, vd = device_tensors(q, k, v, dtype)
     _, w1, s1, t1 = sa.solattn_forward_debug(qd, kd, vd, None, 128, 1.25)
     w2, s2, t2 = sa.solattn_route(qd, kd, vd, 128, 1.25)
     torch.cuda.synchronize()
