@@ -39,10 +39,14 @@
 //     is checked once at the end.  If some row's first half has no finite
 //     logit, or some denominator ends above 2^64 (or inf / NaN), the fast
 //     path's result is discarded and the query block is recomputed from
-//     the start by the rescaling path (VGPR
-//     accumulators, lazy rescale when the maximum grows by more than 2^8).  The denominator adds the
+//     the start by the rescaling path (VGPR accumulators, lazy rescale when
+//     the maximum grows by more than 2^8).  The denominator adds the
 //     bf16-rounded weights the MFMA consumes (v_dot2 against (1, 1)), so
 //     numerator and denominator agree;
+//   * the routing prologue issues the query block's Q loads between its
+//     score pass and its keep-mask pass, so they arrive under the latter;
+//     the epilogue writes each output row with 16-byte stores after a
+//     v_permlane32_swap between the lane halves;
 //   * workgroups are remapped so that the query blocks of one head run on
 //     one XCD and share its L2 for the K/V tiles they keep.
 #include "common.h"
