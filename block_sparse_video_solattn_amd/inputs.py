@@ -198,3 +198,56 @@ def logit_jump(B, H, N, D, dtype="bf16", jump_block=5, scale=6.0, seed=0) -> tup
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     return q, k, v
 
+
+
+def rope_tables(N: int, prefix_len: int, grid: tuple, rope_dim: int,
+                base: float = 10000.0) -> tuple:
+    """Synthetic per-token rotary angle tables (cos, sin), float32 [N][rope_dim/2].
+
+    A stand-in for a video model's 3-D position encoding: the rope_dim/2
+    channel pairs are split over the (t, y, x) axes of the latent grid (a
+    quarter each to t, the rest shared by y and x), pair i of an axis with
+    n pairs turning at base^(-i/n) radians per grid step; prefix tokens sit
+    at the origin (angle 0).  Only position data: the rotation itself is the
+    producer's."""
+    half = rope_dim // 2
+    nt = half // 4
+    ny = (half - nt) // 2
+    nx = half - nt - ny
+    pos = np.zeros((N, 3), np.float64)
+    pos[prefix_len:] = video_positions(N - prefix_len, grid)
+    ang = np.zeros((N, half), np.float64)
+    col = 0
+    for axis, n in enumerate((nt, ny, nx)):
+        if n:
+            omega = base ** (-np.arange(n, dtype=np.float64) / n)
+            ang[:, col:col + n] = pos[:, axis:axis + 1] * omega[None, :]
+        col += n
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def producer_inputs(B, H, N, D, dtype="bf16", prefix_len=0, grid=None, rope_dim=None,
+                    seed=0) -> dict:
+    """Inputs of the fused Q/K producer: pre-norm q and k, v, the two norm
+    weights and the rotary tables.
+
+    q, k, v come from ``custom`` (field kind when a grid is given); every
+    q / k row is then multiplied by its own scale 10^u, u ~ U(-2, 1.5), so
+    that rows span several decades (pre-norm activations) and eps matters
+    for the smallest.  gamma_q, gamma_k: 1 + N(0, 0.2^2) per channel (a
+    trained norm weight's spread), float32.  rope_dim defaults to d/2
+    (partial RoPE); tables from ``rope_tables`` over the grid."""
+    kind = "field" if grid is not None else "iid_qk_offset"
+    q, k, v = custom(B, H, N, D, dtype, prefix_len, seed, kind=kind, grid=grid)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x51AC])))
+    for x in (q, k):
+        x *= (10.0 ** rng.uniform(-2.0, 1.5, size=x.shape[:-1] + (1,))).astype(np.float32)
+    if dtype == "bf16":
+        q, k = round_to_bf16(q), round_to_bf16(k)
+    gq = (1.0 + 0.2 * rng.standard_normal(D)).astype(np.float32)
+    gk = (1.0 + 0.2 * rng.standard_normal(D)).astype(np.float32)
+    r = D // 2 if rope_dim is None else rope_dim
+    if grid is None:
+        grid = (1, 1, max(1, N - prefix_len))
+    cos, sin = rope_tables(N, prefix_len, grid, r)
+    return dict(q=q, k=k, v=v, gamma_q=gq, gamma_k=gk, rope_dim=r, cos=cos, sin=sin)
