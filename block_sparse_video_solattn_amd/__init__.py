@@ -14,6 +14,7 @@ _BINDING_NAMES = (
     "solattn_version", "solattn_workspace_bytes", "unpack_mask", "raw_call",
     "solattn_transport_record_bytes", "solattn_pack_qkv_int8", "solattn_unpack_qkv_int8",
     "solattn_pack_out_fp8", "solattn_unpack_out_fp8",
+    "solattn_qknorm_rope", "solattn_prepare_qknorm_rope_ws",
 )
 
 

@@ -56,6 +56,10 @@ _SIGS = {
     "solattn_unpack_qkv_int8": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I),
     "solattn_pack_out_fp8": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _P], _I),
     "solattn_unpack_out_fp8": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _P], _I),
+    "solattn_qknorm_rope": ([_P, _P, _P, _P, _F, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I,
+                             _P], _I),
+    "solattn_prepare_qknorm_rope_ws": ([_P, _P, _P, _P, _P, _F, _I64, _P, _P, _P, _P, _I64, _I64,
+                                        _I64, _I64, _I, _I, _P, _SZ, _P], _I),
     "solattn_strerror": ([_I], ctypes.c_char_p),
     "solattn_last_error": ([], ctypes.c_char_p),
     "solattn_version": ([], ctypes.c_char_p),
@@ -100,12 +104,14 @@ def _ptr(t) -> Optional[int]:
 
 
 def _dtype_code(t) -> int:
+    """Element type code of a tensor or a torch.dtype."""
     import torch
-    if t.dtype == torch.bfloat16:
+    dt = t if isinstance(t, torch.dtype) else t.dtype
+    if dt == torch.bfloat16:
         return BF16
-    if t.dtype == torch.float32:
+    if dt == torch.float32:
         return F32
-    raise TypeError("q/k/v must be float32 or bfloat16, got %s" % t.dtype)
+    raise TypeError("q/k/v must be float32 or bfloat16, got %s" % dt)
 
 
 def _mode_code(mode) -> int:
@@ -327,3 +333,55 @@ def solattn_unpack_out_fp8(recv, d: int, o=None, stream=None):
         o = torch.empty((B, P * Hp, Ns, d), dtype=torch.bfloat16, device=recv.device)
     _check(_lib.solattn_unpack_out_fp8(_ptr(recv), B, Hp, Ns, int(d), P, _ptr(o), _stream(stream)))
     return o
+
+
+# ------------------------------------------------------------ fused Q/K producer
+def _f32_vec(t, n, name):
+    import torch
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+        raise ValueError("%s must be a contiguous float32 tensor of %d elements" % (name, n))
+    return t
+
+
+def _producer_ptrs(q, gamma_q, gamma_k, rope_dim, rope_cos, rope_sin):
+    B, H, N, d = _shape(q)
+    _f32_vec(gamma_q, d, "gamma_q")
+    _f32_vec(gamma_k, d, "gamma_k")
+    if rope_dim > 0:
+        _f32_vec(rope_cos, N * (rope_dim // 2), "rope_cos")
+        _f32_vec(rope_sin, N * (rope_dim // 2), "rope_sin")
+    return B, H, N, d
+
+
+def solattn_qknorm_rope(q, k, gamma_q, gamma_k, eps: float, rope_dim: int, rope_cos=None,
+                        rope_sin=None, q_out=None, k_out=None, stream=None):
+    """q', k' = partial RoPE of the RMS-normalised q, k (the producer alone).
+    gamma_*: float32 [d] or None (ones); rope_cos / rope_sin: float32 [N, rope_dim/2]."""
+    B, H, N, d = _producer_ptrs(q, gamma_q, gamma_k, rope_dim, rope_cos, rope_sin)
+    q_out = q.new_empty(q.shape) if q_out is None else q_out
+    k_out = q.new_empty(q.shape) if k_out is None else k_out
+    _check_like(q, k, q_out, k_out)
+    _check(_lib.solattn_qknorm_rope(_ptr(q), _ptr(k), _ptr(gamma_q), _ptr(gamma_k), float(eps),
+                                    int(rope_dim), _ptr(rope_cos), _ptr(rope_sin), _ptr(q_out),
+                                    _ptr(k_out), B, H, N, d, _dtype_code(q), _stream(stream)))
+    return q_out, k_out
+
+
+def solattn_prepare_qknorm_rope_ws(q, k, v, gamma_q, gamma_k, eps: float, rope_dim: int,
+                                   rope_cos, rope_sin, mode, ws, q_out=None, k_out=None,
+                                   want_k_out: bool = True, stream=None):
+    """The producer fused with pooling: writes q' (and k' unless want_k_out
+    is False and no k_out is given; bf16 only) and fills ws as
+    solattn_prepare_ws(q', k', v) would.  Returns (q_out, k_out or None)."""
+    B, H, N, d = _producer_ptrs(q, gamma_q, gamma_k, rope_dim, rope_cos, rope_sin)
+    q_out = q.new_empty(q.shape) if q_out is None else q_out
+    if k_out is None and want_k_out:
+        k_out = q.new_empty(q.shape)
+    _check_like(q, k, v, q_out, k_out)
+    _check(_lib.solattn_prepare_qknorm_rope_ws(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gamma_q), _ptr(gamma_k), float(eps), int(rope_dim),
+        _ptr(rope_cos), _ptr(rope_sin), _ptr(q_out), _ptr(k_out), B, H, N, d, _mode_code(mode),
+        _dtype_code(q), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return q_out, k_out

@@ -14,6 +14,7 @@
 // tile once more for bf16).
 #include "common.h"
 #include "launch.h"
+#include "producer.h"
 
 namespace solattn {
 
@@ -102,13 +103,26 @@ __device__ inline void write_value_tile(const bf16 (*tile)[D + 8], bf16* dst, in
     }
 }
 
+// Pooled key `kk` of a 64-key tile, channel dcol, into the operand-ordered
+// pooled key and value tiles.
+template <int D>
+__device__ inline void put_pooled_kv(bf16* kbarP, bf16* vbarP, int kk, int dcol, float km,
+                                     float vm) {
+    constexpr int KS = D / 16;
+    // key: row kk of the tile, column dcol
+    const int s = dcol / 16, half = (dcol / 8) & 1, e = dcol & 7;
+    kbarP[ktile_offset(KS, kk / 32, s, 32 * half + (kk & 31), e)] = to_bf16(km);
+    int vs, vh, ve;
+    vtile_slot(kk, &vs, &vh, &ve);
+    vbarP[vtile_offset(dcol / 32, vs, 32 * vh + (dcol & 31), ve)] = to_bf16(vm);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     constexpr int VEC = Vec16<T>::n;
     constexpr int CPR = D / VEC;
     constexpr int RPP = 256 / CPR;
     constexpr int PASSES = 64 / RPP;
-    constexpr int KS = D / 16;
     __shared__ float red[RPP * D];
     __shared__ float mean[D];
     __shared__ bf16 tile[64][D + 8];  // staging for the operand relayout (bf16 only)
@@ -123,12 +137,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     bf16* kbarP = bf ? reinterpret_cast<bf16*>(a.kbarP) + (bh * (Nbp / 64) + j / 64) * D * 64 : nullptr;
     bf16* vbarP = bf ? reinterpret_cast<bf16*>(a.vbarP) + (bh * (Nbp / 64) + j / 64) * D * 64 : nullptr;
     auto put_pooled = [&](int dcol, float km, float vm) {
-        // key: row kk of the tile, column dcol
-        const int s = dcol / 16, half = (dcol / 8) & 1, e = dcol & 7;
-        kbarP[ktile_offset(KS, kk / 32, s, 32 * half + (kk & 31), e)] = to_bf16(km);
-        int vs, vh, ve;
-        vtile_slot(kk, &vs, &vh, &ve);
-        vbarP[vtile_offset(dcol / 32, vs, 32 * vh + (dcol & 31), ve)] = to_bf16(vm);
+        put_pooled_kv<D>(kbarP, vbarP, kk, dcol, km, vm);
     };
 
     if (j >= Nb) {
@@ -193,6 +202,267 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
         __syncthreads();
         write_value_tile<D>(tile, reinterpret_cast<bf16*>(a.vP) + (bh * Nb + j) * (int64_t)D * 64, tid);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Fused Q/K producer: QKNorm then partial RoPE on each Q and K row, the
+// results stored in the input's element type, and the block pooling of the
+// same workgroup taken from those stored values (page "MiniMax 官宣 NVIDIA Sol
+// 团队 H3 加速:5 秒视频 1.653 秒生成并开源", section "提速来自流水线每一段的
+// 叠加", fused-operator item: QKNorm + partial RoPE with the intermediates
+// kept on chip; page "NVIDIA 與 SANA Sol-Engine" news, section "技術組成").
+//
+// Per row of d channels: y = x / sqrt(mean(x^2) + eps) * gamma, then channel
+// pairs (2i, 2i+1) with i < rope_half turn by the tabulated angle of the
+// row's token: (y0, y1) -> (y0 c - y1 s, y0 s + y1 c).  Arithmetic in fp32,
+// one rounding to the element type at the end.  A row is held by CPR
+// consecutive lanes (16 bytes each); its sum of squares is an xor butterfly
+// over those lanes, so every lane normalises with the same bits.  Pooling
+// then sums the rounded values in the order pool_kernel sums loaded ones, so
+// the workspace equals the one pool_kernel leaves for the stored q', k'.
+
+template <typename T, int D>
+struct RowProducer {
+    static constexpr int VEC = Vec16<T>::n;
+    static constexpr int CPR = D / VEC;
+    static constexpr int PAIRS = VEC / 2;
+    float g[VEC];  // norm weight of this thread's channels
+    const float* cosp;
+    const float* sinp;
+    int rope_half, vec_tables, c;
+    float eps;
+
+    __device__ RowProducer(const float* gamma, const ProducerArgs& p, int tid) {
+        c = tid % CPR;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) g[e] = gamma ? gamma[c * VEC + e] : 1.f;
+        cosp = p.rope_cos;
+        sinp = p.rope_sin;
+        rope_half = p.rope_half;
+        vec_tables = p.vec_tables;
+        eps = p.eps;
+    }
+
+    // Rotation angles of this thread's pairs in the row of token t: table
+    // entries where the row lies inside the sequence (valid) and the pair is
+    // rotated, else cos 1, sin 0 (an exact identity).
+    __device__ void load_angles(int64_t t, bool valid, float (&cs)[PAIRS],
+                                float (&sn)[PAIRS]) const {
+        const int p0 = c * PAIRS;  // first pair of this thread
+#pragma unroll
+        for (int i = 0; i < PAIRS; ++i) cs[i] = 1.f, sn[i] = 0.f;
+        if (!valid || p0 >= rope_half) return;
+        const int64_t o = t * rope_half + p0;
+        if (vec_tables) {
+            // rope_half is a multiple of PAIRS and the tables are aligned to
+            // PAIRS floats: this thread's pairs are one vector each
+            if constexpr (PAIRS == 4) {
+                const f32x4 cv = *reinterpret_cast<const f32x4*>(cosp + o);
+                const f32x4 sv = *reinterpret_cast<const f32x4*>(sinp + o);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) cs[i] = cv[i], sn[i] = sv[i];
+            } else {
+                const f32x2 cv = *reinterpret_cast<const f32x2*>(cosp + o);
+                const f32x2 sv = *reinterpret_cast<const f32x2*>(sinp + o);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) cs[i] = cv[i], sn[i] = sv[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PAIRS; ++i) {
+                if (p0 + i < rope_half) {
+                    cs[i] = cosp[o + i];
+                    sn[i] = sinp[o + i];
+                }
+            }
+        }
+    }
+
+    // x: this thread's chunk of one row (zeros past the sequence end); cs,
+    // sn: its angles.  Leaves the rounded result in x.
+    __device__ void apply(typename Vec16<T>::type& x, const float (&cs)[PAIRS],
+                          const float (&sn)[PAIRS]) const {
+        float y[VEC];
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            y[e] = (float)x[e];
+            ss = __builtin_fmaf(y[e], y[e], ss);
+        }
+#pragma unroll
+        for (int m = 1; m < CPR; m <<= 1) ss += __shfl_xor(ss, m);
+        const float rinv = 1.f / sqrtf(ss * (1.f / (float)D) + eps);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) y[e] = y[e] * rinv * g[e];
+        const int p0 = c * PAIRS;
+#pragma unroll
+        for (int i = 0; i < PAIRS; ++i) {
+            if (p0 + i < rope_half) {
+                const float a0 = y[2 * i], a1 = y[2 * i + 1];
+                y[2 * i] = a0 * cs[i] - a1 * sn[i];
+                y[2 * i + 1] = a0 * sn[i] + a1 * cs[i];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[e] = (T)y[e];
+    }
+};
+
+// load_rows with the producer applied to every row before it is summed and
+// kept; the produced rows inside the sequence are stored to `out` (if any).
+// All of the thread's row chunks and angles are loaded before the first row
+// is produced, so their latencies overlap.
+template <typename T, int D>
+__device__ inline void produce_rows(const T* __restrict__ base, T* __restrict__ out, int n,
+                                    int64_t t0, int tid, const RowProducer<T, D>& prod,
+                                    float (&acc)[Vec16<T>::n], typename Vec16<T>::type* keep) {
+    constexpr int VEC = Vec16<T>::n;
+    constexpr int CPR = D / VEC;
+    constexpr int RPP = 256 / CPR;
+    constexpr int PASSES = 64 / RPP;
+    constexpr int PAIRS = RowProducer<T, D>::PAIRS;
+    const int c = tid % CPR, r0 = tid / CPR;
+    typename Vec16<T>::type xs[PASSES];
+    float cs[PASSES][PAIRS], sn[PASSES][PAIRS];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int r = r0 + p * RPP;
+        if (r < n) {
+            xs[p] = *reinterpret_cast<const typename Vec16<T>::type*>(base + (int64_t)r * D + c * VEC);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) xs[p][e] = (T)0.f;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) prod.load_angles(t0 + r0 + p * RPP, r0 + p * RPP < n, cs[p], sn[p]);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int r = r0 + p * RPP;
+        typename Vec16<T>::type x = xs[p];
+        prod.apply(x, cs[p], sn[p]);
+        if (out && r < n)
+            *reinterpret_cast<typename Vec16<T>::type*>(out + (int64_t)r * D + c * VEC) = x;
+        if (keep) keep[p] = x;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += (float)x[e];
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void produce_pool_kernel(PoolArgs a, ProducerArgs pr) {
+    constexpr int VEC = Vec16<T>::n;
+    constexpr int CPR = D / VEC;
+    constexpr int RPP = 256 / CPR;
+    constexpr int PASSES = 64 / RPP;
+    __shared__ float red[RPP * D];
+    __shared__ float mean[D];
+    __shared__ bf16 tile[64][D + 8];
+
+    const int tid = threadIdx.x;
+    // token blocks run fastest through the grid, as in pool_kernel: one head
+    // streams through contiguous memory at a time, and with the block count a
+    // multiple of eight each XCD serves the same eighth of the blocks -- and
+    // of the rotary table rows -- for every head, so those rows stay in its L2
+    // from one head to the next (measured 15 % faster than heads-fastest)
+    const int64_t j = blockIdx.x, bh = blockIdx.y;
+    const int64_t Nb = a.Nb, Nbp = a.Nbp, N = a.N;
+    const bool bf = a.dtype == kBF16;
+    const int kk = (int)(j & 63);
+    const bool pooled_tiles = bf && a.pooled;
+    bf16* kbarP = pooled_tiles ? reinterpret_cast<bf16*>(a.kbarP) + (bh * (Nbp / 64) + j / 64) * D * 64 : nullptr;
+    bf16* vbarP = pooled_tiles ? reinterpret_cast<bf16*>(a.vbarP) + (bh * (Nbp / 64) + j / 64) * D * 64 : nullptr;
+
+    if (j >= Nb) {
+        // padding of the pooled tiles, as in pool_kernel
+        if (!a.pooled) return;
+        if (tid < D) {
+            a.kbarT[(bh * D + tid) * Nbp + j] = 0.f;
+            if (bf) put_pooled_kv<D>(kbarP, vbarP, kk, tid, 0.f, 0.f);
+        }
+        return;
+    }
+
+    const int n = (int)((j + 1) * 64 <= N ? 64 : N - j * 64);
+    const int64_t row0 = bh * N + j * 64;
+    const bool pack = bf && a.pack;
+    float acc[VEC];
+    typename Vec16<T>::type keep[PASSES];
+    auto stage = [&]() {
+        const int c = tid % CPR, r0 = tid / CPR;
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) tile[r0 + p * RPP][c * VEC + e] = (bf16)keep[p][e];
+    };
+
+    // Q': stored; its block mean
+    {
+        const RowProducer<T, D> prod(pr.gamma_q, pr, tid);
+        produce_rows<T, D>(reinterpret_cast<const T*>(a.q) + row0 * D,
+                           reinterpret_cast<T*>(pr.q_out) + row0 * D, n, j * 64, tid, prod, acc,
+                           nullptr);
+    }
+    if (a.pooled) {
+        reduce_mean<T, D>(acc, n, tid, red, mean);
+        if (tid < D) a.qbar[(bh * Nb + j) * D + tid] = mean[tid];
+    }
+    // K': stored if asked; means and the operand-ordered key tile
+    {
+        const RowProducer<T, D> prod(pr.gamma_k, pr, tid);
+        T* ko = pr.k_out ? reinterpret_cast<T*>(pr.k_out) + row0 * D : nullptr;
+        produce_rows<T, D>(reinterpret_cast<const T*>(a.k) + row0 * D, ko, n, j * 64, tid, prod,
+                           acc, keep);
+    }
+    if (a.pooled) {
+        reduce_mean<T, D>(acc, n, tid, red, mean);
+        if (tid < D) {
+            a.kbar[(bh * Nb + j) * D + tid] = mean[tid];
+            a.kbarT[(bh * D + tid) * Nbp + j] = mean[tid];
+        }
+    }
+    if (pack) {
+        stage();
+        __syncthreads();
+        write_key_tile<D>(tile, reinterpret_cast<bf16*>(a.kP) + (bh * Nb + j) * (int64_t)D * 64, tid);
+        __syncthreads();
+    }
+    if (!a.pooled && !pack) return;  // the producer alone
+    // V: as pool_kernel
+    load_rows<T, D>(reinterpret_cast<const T*>(a.v) + row0 * D, n, tid, acc, keep);
+    if (a.pooled) {
+        const float km = tid < D ? mean[tid] : 0.f;  // K mean, still in LDS
+        __syncthreads();
+        reduce_mean<T, D>(acc, n, tid, red, mean);
+        if (tid < D) {
+            a.vbar[(bh * Nb + j) * D + tid] = mean[tid];
+            if (bf) put_pooled_kv<D>(kbarP, vbarP, kk, tid, km, mean[tid]);
+        }
+    }
+    if (pack) {
+        stage();
+        __syncthreads();
+        write_value_tile<D>(tile, reinterpret_cast<bf16*>(a.vP) + (bh * Nb + j) * (int64_t)D * 64, tid);
+    }
+}
+
+hipError_t launch_produce_pool(const PoolArgs& a, const ProducerArgs& p, int64_t BH,
+                               hipStream_t s) {
+    const dim3 grid((unsigned)(a.pooled ? a.Nbp : a.Nb), (unsigned)BH);
+    if (a.dtype == kBF16) {
+        if (a.d == 128)
+            hipLaunchKernelGGL((produce_pool_kernel<bf16, 128>), grid, dim3(256), 0, s, a, p);
+        else
+            hipLaunchKernelGGL((produce_pool_kernel<bf16, 64>), grid, dim3(256), 0, s, a, p);
+    } else {
+        if (a.d == 128)
+            hipLaunchKernelGGL((produce_pool_kernel<float, 128>), grid, dim3(256), 0, s, a, p);
+        else
+            hipLaunchKernelGGL((produce_pool_kernel<float, 64>), grid, dim3(256), 0, s, a, p);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_pool(const PoolArgs& a, int64_t BH, hipStream_t s) {

@@ -13,8 +13,10 @@
 
 #include "../../include/solattn.h"
 #include "../../include/solattn_probe.h"
+#include "../../include/solattn_producer.h"
 #include "../../include/solattn_transport.h"
 #include "launch.h"
+#include "producer.h"
 
 using namespace solattn;
 
@@ -48,9 +50,10 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 // Every check happens here, on the host, before any device call.
 int validate(const void* q, const void* k, const void* v, const void* out, bool need_out,
              int64_t B, int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau, int mode,
-             int dtype) {
+             int dtype, bool kv_optional = false) {
     g_last_error.clear();
-    if (!q || !k || !v) return fail(SOLATTN_EINVAL, "q, k and v must be non-NULL");
+    if (!q) return fail(SOLATTN_EINVAL, "q must be non-NULL");
+    if (!kv_optional && (!k || !v)) return fail(SOLATTN_EINVAL, "q, k and v must be non-NULL");
     if (need_out && !out) return fail(SOLATTN_EINVAL, "out must be non-NULL");
     if (B < 1 || H < 1 || N < 1)
         return fail(SOLATTN_EINVAL, "B, H, N must be >= 1 (got %lld, %lld, %lld)", (long long)B,
@@ -82,8 +85,8 @@ int validate(const void* q, const void* k, const void* v, const void* out, bool 
         return fail(SOLATTN_EUNSUPPORTED, "B*H*ceil(N/64) exceeds 2^31 workgroups");
     if (out) {
         const size_t bytes = (size_t)B * H * N * d * (dtype == SOLATTN_BF16 ? 2 : 4);
-        if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
-            overlaps(out, bytes, v, bytes))
+        if (overlaps(out, bytes, q, bytes) || (k && overlaps(out, bytes, k, bytes)) ||
+            (v && overlaps(out, bytes, v, bytes)))
             return fail(SOLATTN_EINVAL, "out must not overlap q, k or v");
     }
     return SOLATTN_OK;
@@ -164,8 +167,8 @@ int internal_ws(size_t need, void** out) {
 
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
-int run_prepare(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t N,
-                int64_t d, int mode, int dtype, void* ws, hipStream_t s, bool pack) {
+PoolArgs pool_args(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t N,
+                   int64_t d, int mode, int dtype, void* ws, bool pack) {
     const WsLayout L = ws_layout(B, H, N, d, dtype);
     PoolArgs p;
     p.q = q;
@@ -186,6 +189,12 @@ int run_prepare(const void* q, const void* k, const void* v, int64_t B, int64_t 
     p.dtype = dtype;
     p.pooled = (mode & SOLATTN_MODE_MASK) != SOLATTN_DENSE;
     p.pack = pack && dtype == kBF16;
+    return p;
+}
+
+int run_prepare(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t N,
+                int64_t d, int mode, int dtype, void* ws, hipStream_t s, bool pack) {
+    const PoolArgs p = pool_args(q, k, v, B, H, N, d, mode, dtype, ws, pack);
     if (!p.pooled && !p.pack) return SOLATTN_OK;  // fp32 dense: nothing to prepare
     hipError_t e = launch_pool(p, B * H, s);
     if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
@@ -247,9 +256,104 @@ int check_ws(void* ws, size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t
     return SOLATTN_OK;
 }
 
+// Producer arguments (shapes were checked by validate()): weights, eps,
+// rotary tables, the outputs and their overlaps.
+int check_producer(const void* q, const void* k, const void* v, const float* gq,
+                   const float* gk, float eps, int64_t rope_dim, const float* rc,
+                   const float* rs, void* q_out, void* k_out, bool k_out_optional,
+                   int64_t B, int64_t H, int64_t N, int64_t d, int dtype, ProducerArgs* pa) {
+    if (!(eps > 0.f) || std::isinf(eps))
+        return fail(SOLATTN_EINVAL, "eps must be finite and > 0 (got %g)", (double)eps);
+    if (rope_dim < 0 || rope_dim > d || (rope_dim & 1))
+        return fail(SOLATTN_EINVAL, "rope_dim must be even and in [0, d] (got %lld)",
+                    (long long)rope_dim);
+    if (rope_dim > 0 && (!rc || !rs))
+        return fail(SOLATTN_EINVAL, "rope_cos and rope_sin must be non-NULL when rope_dim > 0");
+    auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+    if (!al4(gq) || !al4(gk) || (rope_dim > 0 && (!al4(rc) || !al4(rs))))
+        return fail(SOLATTN_EINVAL, "norm weights and rotary tables must be 4-byte aligned");
+    if (!q_out || (!k_out && !k_out_optional))
+        return fail(SOLATTN_EINVAL, k_out_optional ? "q_out must be non-NULL"
+                                                   : "q_out and k_out must be non-NULL");
+    if (!aligned16(q_out) || !aligned16(k_out))
+        return fail(SOLATTN_EINVAL, "q_out and k_out must be 16-byte aligned");
+    const size_t tb = (size_t)B * H * N * d * (dtype == SOLATTN_BF16 ? 2 : 4);
+    const size_t gb = (size_t)d * 4, tab = (size_t)N * (size_t)(rope_dim / 2) * 4;
+    for (const void* o : {q_out, k_out}) {
+        if (!o) continue;
+        for (const void* i : {q, k, v})
+            if (i && overlaps(o, tb, i, tb))
+                return fail(SOLATTN_EINVAL, "q_out and k_out must not overlap q, k or v");
+        if ((gq && overlaps(o, tb, gq, gb)) || (gk && overlaps(o, tb, gk, gb)) ||
+            (tab && (overlaps(o, tb, rc, tab) || overlaps(o, tb, rs, tab))))
+            return fail(SOLATTN_EINVAL, "q_out and k_out must not overlap the weights or tables");
+    }
+    if (k_out && overlaps(q_out, tb, k_out, tb))
+        return fail(SOLATTN_EINVAL, "q_out and k_out must not overlap each other");
+    const int pairs = dtype == SOLATTN_BF16 ? 4 : 2;  // rotary pairs per thread chunk
+    const uintptr_t vmask = (uintptr_t)pairs * 4 - 1;
+    pa->gamma_q = gq;
+    pa->gamma_k = gk;
+    pa->rope_cos = rope_dim > 0 ? rc : nullptr;
+    pa->rope_sin = rope_dim > 0 ? rs : nullptr;
+    pa->q_out = q_out;
+    pa->k_out = k_out;
+    pa->eps = eps;
+    pa->rope_half = (int)(rope_dim / 2);
+    pa->vec_tables = rope_dim > 0 && (rope_dim / 2) % pairs == 0 &&
+                     (reinterpret_cast<uintptr_t>(rc) & vmask) == 0 &&
+                     (reinterpret_cast<uintptr_t>(rs) & vmask) == 0;
+    return SOLATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int solattn_qknorm_rope(const void* q, const void* k, const float* gamma_q,
+                        const float* gamma_k, float eps, int64_t rope_dim,
+                        const float* rope_cos, const float* rope_sin, void* q_out, void* k_out,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int dtype, void* stream) {
+    // v is not read: q stands in for it in the shared shape checks
+    int rc = validate(q, k, q, nullptr, false, B, H, N, d, 0, 0.f, SOLATTN_DENSE, dtype);
+    if (rc) return rc;
+    ProducerArgs pa;
+    if ((rc = check_producer(q, k, nullptr, gamma_q, gamma_k, eps, rope_dim, rope_cos, rope_sin,
+                             q_out, k_out, false, B, H, N, d, dtype, &pa)))
+        return rc;
+    PoolArgs p = {};
+    p.q = q;
+    p.k = k;
+    p.N = N;
+    p.Nb = (N + 63) / 64;
+    p.Nbp = (p.Nb + 63) / 64 * 64;
+    p.d = (int)d;
+    p.dtype = dtype;
+    p.pooled = 0;
+    p.pack = 0;
+    hipError_t e = launch_produce_pool(p, pa, B * H, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "producer kernel launch");
+    return SOLATTN_OK;
+}
+
+int solattn_prepare_qknorm_rope_ws(const void* q, const void* k, const void* v,
+                                   const float* gamma_q, const float* gamma_k, float eps,
+                                   int64_t rope_dim, const float* rope_cos,
+                                   const float* rope_sin, void* q_out, void* k_out, int64_t B,
+                                   int64_t H, int64_t N, int64_t d, int mode, int dtype,
+                                   void* ws, size_t ws_bytes, void* stream) {
+    int rc = validate(q, k, v, nullptr, false, B, H, N, d, 0, 0.f, mode, dtype);
+    if (rc) return rc;
+    if ((rc = check_ws(ws, ws_bytes, B, H, N, d, dtype))) return rc;
+    ProducerArgs pa;
+    if ((rc = check_producer(q, k, v, gamma_q, gamma_k, eps, rope_dim, rope_cos, rope_sin, q_out,
+                             k_out, dtype == SOLATTN_BF16, B, H, N, d, dtype, &pa)))
+        return rc;
+    const PoolArgs p = pool_args(q, k, v, B, H, N, d, mode, dtype, ws, true);
+    hipError_t e = launch_produce_pool(p, pa, B * H, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "producer kernel launch");
+    return SOLATTN_OK;
+}
 
 size_t solattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
     if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128) || (dtype != 0 && dtype != 1)) return 0;
@@ -292,7 +396,9 @@ int solattn_prepare_ws(const void* q, const void* k, const void* v, int64_t B, i
 int solattn_attend_ws(const void* q, const void* k, const void* v, void* out, int64_t B,
                       int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau, int mode,
                       int dtype, void* ws, size_t ws_bytes, void* stream) {
-    int rc = validate(q, k, v, out, true, B, H, N, d, prefix_len, tau, mode, dtype);
+    // the bf16 attention reads keys and values from the workspace only
+    int rc = validate(q, k, v, out, true, B, H, N, d, prefix_len, tau, mode, dtype,
+                      dtype == SOLATTN_BF16);
     if (rc) return rc;
     if ((rc = check_ws(ws, ws_bytes, B, H, N, d, dtype))) return rc;
     return run_attend(q, k, v, out, B, H, N, d, prefix_len, tau, mode, dtype, ws,

@@ -144,3 +144,41 @@ def test_transport_entry_points_validate(lib):
     assert lib.raw_call("solattn_pack_out_fp8", X, 1, 2, 64, 64, 2, None, None) == 1
     assert lib.raw_call("solattn_unpack_out_fp8", S, 1, 2, 64, 32, 2, X, None) == 1
     assert lib.solattn_last_error() != ""
+
+
+def test_producer_entry_points_validate(lib):
+    # every rejection happens on the host, before any device call
+    f = ctypes.c_float
+    X, Y, Z, QO, KO, G, C, S, W = (A, A + 0x1000000, A + 0x2000000, A + 0x3000000,
+                                   A + 0x4000000, A + 0x5000000, A + 0x6000000, A + 0x7000000,
+                                   A + 0x8000000)
+
+    def alone(q=X, k=Y, gq=G, gk=G, eps=1e-6, r=64, c=C, s=S, qo=QO, ko=KO, N=1024, d=128,
+              dtype=1):
+        return lib.raw_call("solattn_qknorm_rope", q, k, gq, gk, f(eps), r, c, s, qo, ko,
+                            1, 2, N, d, dtype, None)
+
+    def fused(q=X, k=Y, v=Z, eps=1e-6, r=64, c=C, s=S, qo=QO, ko=KO, mode=1, dtype=1,
+              ws=W, ws_bytes=1 << 30):
+        return lib.raw_call("solattn_prepare_qknorm_rope_ws", q, k, v, G, G, f(eps), r, c, s,
+                            qo, ko, 1, 2, 1024, 128, mode, dtype, ws, ws_bytes, None)
+
+    for bad in (dict(eps=0.0), dict(eps=-1e-6), dict(eps=math.inf), dict(eps=math.nan),
+                dict(r=63), dict(r=130), dict(r=-2), dict(c=None), dict(s=None),
+                dict(qo=None), dict(ko=None), dict(qo=QO + 8), dict(gq=G + 2),
+                dict(c=C + 1), dict(qo=X + 0x100), dict(ko=QO + 0x100), dict(ko=G - 0x100),
+                dict(d=96), dict(N=0), dict(dtype=2), dict(q=None)):
+        assert alone(**bad) == lib.EINVAL, bad
+        assert lib.solattn_last_error() != ""
+    # no rotation: tables may be NULL; NULL weights mean ones (rejections
+    # above came from the argument named, the rest is accepted up to the
+    # first device call, which these fake addresses never reach)
+    for bad in (dict(ws=None), dict(ws_bytes=16), dict(eps=0.0), dict(mode=5),
+                dict(ko=None, dtype=0), dict(v=None), dict(qo=Z + 0x100)):
+        assert fused(**bad) == lib.EINVAL, bad
+    # bf16 attend reads neither k nor v: NULL accepted past validation, so
+    # probe only the rejections that remain
+    assert lib.raw_call("solattn_attend_ws", None, None, None, A + 0x1000000, 1, 1, 64, 128, 0,
+                        f(1.0), 1, 1, A, 1 << 30, None) == lib.EINVAL
+    assert lib.raw_call("solattn_attend_ws", A, None, None, A + 0x1000000, 1, 1, 64, 128, 0,
+                        f(1.0), 1, 0, A, 1 << 30, None) == lib.EINVAL   # fp32 needs k, v
