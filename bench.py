@@ -288,6 +288,83 @@ def sp_rank_check(sa, stream, q_all, k_all, v_all, prefix_len, tau, P=8):
     return res
 
 
+def producer_check(sa, stream, tau):
+    """The attention step from pre-norm Q/K on the refine shape: QKNorm +
+    partial RoPE (half of the 128 channels rotated, 3-D positions) fused
+    with the pooling pass, then the attention, against the same work unfused
+    (the producer alone writing q' and k', then the plain pooling pass, then
+    the attention).  Inputs: the seeded producer recipe (pre-norm rows over
+    several decades, norm weights near one)."""
+    import numpy as np
+    import torch
+    from block_sparse_video_solattn_amd import inputs
+    w = inputs.WORKLOADS["refine"]
+    B, H, N, d = w.B, w.H, w.N, w.D
+    r = d // 2
+    inp = inputs.producer_inputs(B, H, N, d, "bf16", prefix_len=w.prefix_len, grid=w.grid,
+                                 rope_dim=r, seed=SEED + 7)
+    q, k, v = (torch.from_numpy(inp[n]).to("cuda").to(torch.bfloat16).contiguous()
+               for n in ("q", "k", "v"))
+    gq, gk, cs, sn = (torch.from_numpy(inp[n]).to("cuda").contiguous()
+                      for n in ("gamma_q", "gamma_k", "cos", "sin"))
+    del inp
+    eps = 1e-6
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    out = torch.empty_like(q)
+    ws = torch.empty(sa.solattn_workspace_bytes(B, H, N, d, sa.BF16), dtype=torch.uint8,
+                     device="cuda")
+    t = {
+        "fused_prepare": lambda: sa.solattn_prepare_qknorm_rope_ws(
+            q, k, v, gq, gk, eps, r, cs, sn, "sparse", ws, q_out=qo, want_k_out=False),
+        "fused_prepare_with_k_out": lambda: sa.solattn_prepare_qknorm_rope_ws(
+            q, k, v, gq, gk, eps, r, cs, sn, "sparse", ws, q_out=qo, k_out=ko),
+        "producer_alone": lambda: sa.solattn_qknorm_rope(q, k, gq, gk, eps, r, cs, sn,
+                                                         q_out=qo, k_out=ko),
+        "pool_after_producer": lambda: sa.solattn_prepare_ws(qo, ko, v, "sparse", ws),
+        "attention": lambda: sa.solattn_attend_ws(qo, None, None, out, w.prefix_len, tau,
+                                                  "sparse", ws),
+    }
+    t["producer_alone"]()
+    ms = {}
+    for name, fn in t.items():
+        fn()
+        ms[name] = float(np.median(time_calls(fn, 20, stream)))
+
+    def fused_step():
+        t["fused_prepare"]()
+        t["attention"]()
+
+    def unfused_step():
+        t["producer_alone"]()
+        t["pool_after_producer"]()
+        t["attention"]()
+    fused_step()
+    unfused_step()
+    fs = float(np.median(time_calls(fused_step, 20, stream)))
+    us = float(np.median(time_calls(unfused_step, 20, stream)))
+    words, _, _ = sa.solattn_route(qo, ko, v, w.prefix_len, tau, want_scores=False)
+    torch.cuda.synchronize()
+    pb = (w.prefix_len + 63) // 64
+    m = sa.unpack_mask(words, w.nb)
+    el = B * H * N * d * 2                       # bytes of one bf16 [B,H,N,d] tensor
+    tab = 2 * N * (r // 2) * 4                   # both rotary tables, read once
+    nbytes = {"fused_prepare": pool_bytes(B, H, N, d) + el + tab,
+              "fused_prepare_with_k_out": pool_bytes(B, H, N, d) + 2 * el + tab,
+              "producer_alone": 4 * el + tab,
+              "pool_after_producer": pool_bytes(B, H, N, d)}
+    res = {"workload": "refine shape from pre-norm Q/K: RMS QKNorm (eps 1e-6, weights) + RoPE "
+                       "on %d of %d channels, sparse tau %g" % (r, d, tau),
+           "fused_step_ms": round(fs, 4), "unfused_step_ms": round(us, 4),
+           "fused_saves_ms": round(us - fs, 4),
+           "video_sparsity": round(float(1 - m[..., pb:].mean()), 4)}
+    for name, v_ in ms.items():
+        e = {"ms": round(v_, 4)}
+        if name in nbytes:
+            e["GBps"] = round(nbytes[name] / (v_ * 1e-3) / 1e9, 1)
+        res[name] = e
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -467,6 +544,8 @@ def main():
         res["setup_ms"] = round(float(np.median(time_calls(setup, 20, stream))), 4)
         res["sp_rank_p8"] = sp_rank_check(sa, stream, qd, kd, vd, w.prefix_len, tau)
         del qd, kd, vd, out, ws, dev
+        torch.cuda.empty_cache()
+        res["qk_producer"] = producer_check(sa, stream, tau)
         torch.cuda.empty_cache()
         res["sparsity_90_check"] = draft_check(sa, stream)
         torch.cuda.empty_cache()
