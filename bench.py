@@ -21,6 +21,9 @@ METRIC = "ms/call + dense-equiv TFLOP/s and % bf16 MFMA peak on kept tiles, N=16
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
 SEED = 3000
+# extra legs after the headline measurement, in run order
+LEGS = ("mfma_probe", "dense_sweep", "setup", "sp_rank_p8", "qk_producer", "sparsity_90_check",
+        "long_clip")
 SEED_LONG = 5000
 
 # HBM traffic of one attention dispatch from rocprofv3 counters on this
@@ -372,10 +375,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--tau", type=float, default=1.25)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip dense / tau sweep / setup timing")
+    ap.add_argument("--no-extra", action="store_true", help="skip every extra leg")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated extra legs to run (default all): " + ",".join(LEGS))
     ap.add_argument("--copy-calib", action="store_true",
                     help="run one plain 256 MiB device copy first (counter calibration)")
     args = ap.parse_args()
+    legs = set(LEGS) if args.legs == "all" else set(args.legs.split(","))
+    if legs - set(LEGS):
+        ap.error("unknown legs: %s" % ",".join(sorted(legs - set(LEGS))))
+    if args.no_extra:
+        legs = set()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this operator is measured at one GPU's share; "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -480,7 +490,7 @@ def main():
                      "traffic": attn_traffic_bytes(), "kernel": "attn_bf16_kernel<128>"},
     }
 
-    if not args.no_extra:
+    if "mfma_probe" in legs:
         # in-run matrix-core ceiling: the probe keeps every SIMD's MFMA pipe busy
         # from register operands (the published peak assumes the 2.4 GHz clock)
         # (one wave per SIMD, ~1 ms per launch)
@@ -493,6 +503,7 @@ def main():
         pms = float(np.median(time_calls(probe, 7, stream)))
         res["mfma_peak_measured_tflops"] = round(1024 * 4096 * 16 * 32768 / (pms * 1e-3) / 1e12, 1)
         res["kept_tile_frac_of_measured_peak"] = round(attn_tflops / res["mfma_peak_measured_tflops"], 4)
+    if "dense_sweep" in legs:
         # score entries within 1e-4 of their row threshold (the parity band)
         wn, sc, th0 = sa.solattn_route(qd, kd, vd, w.prefix_len, tau, want_scores=True)
         res["near_threshold_pairs"] = int(((sc - th0[..., None]).abs() <= 1e-4).sum().item())
@@ -534,6 +545,7 @@ def main():
             variants[vm] = {"ms": round(vms, 4), "speedup_vs_dense": round(dms / vms, 2),
                             "video_sparsity": round(float(1 - mv[..., pb:].mean()), 4)}
         res["routing_variants"] = variants
+    if "setup" in legs:
         # routing setup (pooling + scoring/threshold, no attention)
         mw = torch.zeros((B, H, w.nb, (w.nb + 31) // 32), dtype=torch.int32, device="cuda")
         th = torch.zeros((B, H, w.nb), dtype=torch.float32, device="cuda")
@@ -542,13 +554,17 @@ def main():
             sa.solattn_route(qd, kd, vd, w.prefix_len, tau, want_scores=False, mask=mw, thr=th)
         setup()
         res["setup_ms"] = round(float(np.median(time_calls(setup, 20, stream))), 4)
+    if "sp_rank_p8" in legs:
         res["sp_rank_p8"] = sp_rank_check(sa, stream, qd, kd, vd, w.prefix_len, tau)
-        del qd, kd, vd, out, ws, dev
-        torch.cuda.empty_cache()
+    del qd, kd, vd, out, ws, dev
+    torch.cuda.empty_cache()
+    if "qk_producer" in legs:
         res["qk_producer"] = producer_check(sa, stream, tau)
         torch.cuda.empty_cache()
+    if "sparsity_90_check" in legs:
         res["sparsity_90_check"] = draft_check(sa, stream)
         torch.cuda.empty_cache()
+    if "long_clip" in legs:
         res["long_clip"] = long_clip_check(sa, stream)
 
     if not args.no_cpu:
