@@ -99,8 +99,14 @@ def cpu_baseline(q, k, v, w, tau, budget_s=15.0):
         if time.time() - t0 > budget_s:
             break
     dt = time.time() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(dt / heads * w.H * 1000.0, 1), "unit": "ms/call", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": "%d of %d heads of the same refine call (sparse, tau=%g, all query blocks), "
                       "scaled by %d/%d" % (heads, w.H, tau, w.H, heads)}
 
