@@ -448,8 +448,44 @@ __global__ __launch_bounds__(256) void produce_pool_kernel(PoolArgs a, ProducerA
     }
 }
 
-hipError_t launch_produce_pool(const PoolArgs& a, const ProducerArgs& p, int64_t BH,
-                               hipStream_t s) {
+// The pooling grids put the (batch, head) slices on grid y, whose documented
+// limit is 65536: larger counts are launched in ranges of heads, each a
+// launch of its own over pointers advanced to its first head (every per-head
+// region of the inputs and the workspace is contiguous in the slice index).
+constexpr int64_t kMaxGridY = 65535;
+
+template <typename P>
+P* advance(P* p, int64_t bytes) {
+    return p ? reinterpret_cast<P*>(reinterpret_cast<uintptr_t>(p) + bytes) : p;
+}
+
+PoolArgs heads_from(const PoolArgs& a, int64_t h0) {
+    const int64_t es = a.dtype == kBF16 ? 2 : 4, D = a.d;
+    PoolArgs b = a;
+    b.q = advance(a.q, h0 * a.N * D * es);
+    b.k = advance(a.k, h0 * a.N * D * es);
+    b.v = advance(a.v, h0 * a.N * D * es);
+    b.qbar = advance(a.qbar, h0 * a.Nb * D * 4);
+    b.kbar = advance(a.kbar, h0 * a.Nb * D * 4);
+    b.vbar = advance(a.vbar, h0 * a.Nb * D * 4);
+    b.kbarT = advance(a.kbarT, h0 * D * a.Nbp * 4);
+    b.kbarP = advance(a.kbarP, h0 * a.Nbp * D * 2);
+    b.vbarP = advance(a.vbarP, h0 * a.Nbp * D * 2);
+    b.kP = advance(a.kP, h0 * a.Nb * 64 * D * 2);
+    b.vP = advance(a.vP, h0 * a.Nb * 64 * D * 2);
+    return b;
+}
+
+ProducerArgs heads_from(const ProducerArgs& p, const PoolArgs& a, int64_t h0) {
+    const int64_t es = a.dtype == kBF16 ? 2 : 4;
+    ProducerArgs b = p;
+    b.q_out = advance(p.q_out, h0 * a.N * a.d * es);
+    b.k_out = advance(p.k_out, h0 * a.N * a.d * es);
+    return b;
+}
+
+hipError_t launch_produce_pool_heads(const PoolArgs& a, const ProducerArgs& p, int64_t BH,
+                                     hipStream_t s) {
     const dim3 grid((unsigned)(a.pooled ? a.Nbp : a.Nb), (unsigned)BH);
     if (a.dtype == kBF16) {
         if (a.d == 128)
@@ -465,9 +501,8 @@ hipError_t launch_produce_pool(const PoolArgs& a, const ProducerArgs& p, int64_t
     return hipGetLastError();
 }
 
-hipError_t launch_pool(const PoolArgs& a, int64_t BH, hipStream_t s) {
+hipError_t launch_pool_heads(const PoolArgs& a, int64_t BH, hipStream_t s) {
     const dim3 grid((unsigned)(a.pooled ? a.Nbp : a.Nb), (unsigned)BH);
-    if (a.dtype != kBF16 && !a.pooled) return hipSuccess;
     if (a.dtype == kBF16) {
         if (a.d == 128)
             hipLaunchKernelGGL((pool_kernel<bf16, 128>), grid, dim3(256), 0, s, a);
@@ -480,6 +515,26 @@ hipError_t launch_pool(const PoolArgs& a, int64_t BH, hipStream_t s) {
             hipLaunchKernelGGL((pool_kernel<float, 64>), grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_produce_pool(const PoolArgs& a, const ProducerArgs& p, int64_t BH,
+                               hipStream_t s) {
+    for (int64_t h0 = 0; h0 < BH; h0 += kMaxGridY) {
+        const int64_t n = BH - h0 < kMaxGridY ? BH - h0 : kMaxGridY;
+        const hipError_t e = launch_produce_pool_heads(heads_from(a, h0), heads_from(p, a, h0), n, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_pool(const PoolArgs& a, int64_t BH, hipStream_t s) {
+    if (a.dtype != kBF16 && !a.pooled) return hipSuccess;
+    for (int64_t h0 = 0; h0 < BH; h0 += kMaxGridY) {
+        const int64_t n = BH - h0 < kMaxGridY ? BH - h0 : kMaxGridY;
+        const hipError_t e = launch_pool_heads(heads_from(a, h0), n, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace solattn

@@ -335,3 +335,46 @@ def test_invalid_arguments_on_gpu_enqueue_nothing():
         sa.solattn_forward(qd, kd, vd, out, 0, float("nan"))
     torch.cuda.synchronize()
     assert out.abs().max().item() == 0
+
+
+def test_slices_beyond_one_grid_row():
+    # more (batch, head) slices than the pooling grids' y limit (65536): the
+    # pooling passes run in ranges of heads; heads on both sides of each range
+    # boundary are held to the oracle (forward, pooled means, the fused
+    # producer)
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    from oracle import producer as OP
+    B, H, N, d = 1, 65600, 100, 64
+    q, k, v = inputs.custom(B, H, N, d, "bf16", prefix_len=0, seed=77)
+    qd, kd, vd = device_tensors(q, k, v, "bf16")
+    out, words, scores, thr = sa.solattn_forward_debug(qd, kd, vd, None, 0, 0.5, "sparse",
+                                                        want_scores=False)
+    qbar, kbar, vbar = sa.solattn_pool(qd, kd, vd)
+    torch.cuda.synchronize()
+    heads = [0, 1, 65533, 65534, 65535, 65536, 65599]
+    gmask = sa.unpack_mask(words[:, heads], 2)
+    gout = out[0, heads].float().cpu().numpy().astype(np.float64)
+    for n, h in enumerate(heads):
+        r = oracle.head(q[0, h], k[0, h], v[0, h], 0, 0.5,
+                        mask_override=gmask[0, n].astype(np.uint8))
+        assert np.max(np.abs(gout[n] - r["out"])) <= TOL_BF16_ABS, h
+        ro = oracle.head(q[0, h], k[0, h], v[0, h], 0, 0.5, want_out=False)
+        near = np.abs(ro["score"] - ro["thr"][:, None]) <= 1e-4
+        assert not ((gmask[0, n] != ro["mask"].astype(bool)) & ~near).any(), h
+        for got, x in ((qbar, q), (kbar, k), (vbar, v)):
+            ref = np.stack([x[0, h, :64].astype(np.float64).mean(0),
+                            x[0, h, 64:].astype(np.float64).mean(0)])
+            np.testing.assert_allclose(got[0, h].double().cpu().numpy(), ref, rtol=1e-6,
+                                       atol=1e-6)
+    del out, qbar, kbar, vbar
+    # the fused producer over the same slice count (no rotation, weights NULL)
+    ws = torch.empty(sa.solattn_workspace_bytes(B, H, N, d, qd.dtype), dtype=torch.uint8,
+                     device="cuda")
+    qo, _ = sa.solattn_prepare_qknorm_rope_ws(qd, kd, vd, None, None, 1e-6, 0, None, None,
+                                              "sparse", ws, want_k_out=False)
+    torch.cuda.synchronize()
+    for h in heads:
+        exact = OP.qknorm_rope(q[0, h], None, 1e-6)
+        err = np.abs(qo[0, h].double().cpu().numpy() - exact)
+        assert np.all(err <= np.abs(exact) * 2.0 ** -8 + 1e-6), h
