@@ -182,3 +182,45 @@ def test_producer_entry_points_validate(lib):
                         f(1.0), 1, 1, A, 1 << 30, None) == lib.EINVAL
     assert lib.raw_call("solattn_attend_ws", A, None, None, A + 0x1000000, 1, 1, 64, 128, 0,
                         f(1.0), 1, 0, A, 1 << 30, None) == lib.EINVAL   # fp32 needs k, v
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "solattn.h"
+#include "solattn_probe.h"
+#include "solattn_producer.h"
+#include "solattn_transport.h"
+
+int main(void) {
+    /* every call below is rejected on the host before any device call */
+    int rc = solattn_forward(NULL, NULL, NULL, NULL, 1, 1, 64, 64, 0, 1.0f, SOLATTN_SPARSE,
+                             SOLATTN_BF16, NULL);
+    if (rc != SOLATTN_EINVAL || strlen(solattn_last_error()) == 0) return 1;
+    rc = solattn_qknorm_rope(NULL, NULL, NULL, NULL, 1e-6f, 0, NULL, NULL, NULL, NULL, 1, 1, 64,
+                             64, SOLATTN_BF16, NULL);
+    if (rc != SOLATTN_EINVAL) return 2;
+    if (solattn_transport_record_bytes(128) != 144) return 3;
+    if (solattn_workspace_bytes(1, 1, 64, 64, SOLATTN_F32) == 0) return 4;
+    if (solattn_probe_mfma_bf16(NULL, 1, 1, NULL) != SOLATTN_EINVAL) return 5;
+    printf("%s|%s\n", solattn_version(), solattn_strerror(SOLATTN_EUNSUPPORTED));
+    return 0;
+}
+"""
+
+
+def test_headers_compile_as_c_and_link(lib, tmp_path):
+    # the public headers are plain C: a C99 program includes all of them,
+    # links against the library and calls its host-side checks
+    import subprocess
+    src = tmp_path / "use_abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "use_abi"
+    libdir = os.path.dirname(lib.LIB_PATH)
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                           "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                           "-L", libdir, "-lsolattn", "-Wl,-rpath," + libdir])
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    version, err = r.stdout.strip().split("|")
+    assert "gfx950" in version and err == lib.solattn_strerror(2)
