@@ -128,7 +128,9 @@ int solattn_forward_ws(const void* q, const void* k, const void* v, void* out, i
  * can be timed on its own.  solattn_prepare_ws runs step 1 (pooling into the
  * workspace; in DENSE mode only the value-tile relayout the attention kernel
  * reads).  solattn_attend_ws runs steps 2-5 and reads what prepare left in
- * the same workspace for the same q, k, v, shape, dtype and mode.
+ * the same workspace for the same q, k, v, shape, dtype and mode.  For bf16,
+ * solattn_attend_ws reads only q and the workspace (keys and values come
+ * from the tiles prepare wrote): k and v may then be NULL.
  */
 int solattn_prepare_ws(const void* q, const void* k, const void* v, int64_t B, int64_t H,
                        int64_t N, int64_t d, int mode, int dtype, void* ws, size_t ws_bytes,
