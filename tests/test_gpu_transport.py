@@ -134,3 +134,39 @@ def test_exchange_round_trip_on_one_gpu():
         for p in range(P):
             ref_rows = T.dequant_fp8(*T.quant_fp8(to_np_bf16(o_heads[p])[:, :, r * Ns:(r + 1) * Ns]))
             assert np.array_equal(to_np_bf16(oback[r])[:, p * Hp:(p + 1) * Hp], ref_rows)
+
+
+def test_transport_at_the_benchmark_shape():
+    # one rank's share of the 8-GPU refine step that bench.py times: this
+    # rank's 2048-token shard of all 32 heads packed for 8 ranks, a receive
+    # buffer unpacked, 4 heads of output packed and unpacked -- every byte and
+    # value against the oracle
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    P, B, H, Ns, d = 8, 1, 32, 2048, 128
+    Hp = H // P
+    rng = np.random.default_rng(16)
+    q, k, v = (bf16_values(rng, (B, H, Ns, d)) for _ in range(3))
+    send = sa.solattn_pack_qkv_int8(to_dev(q), to_dev(k), to_dev(v), P)
+    torch.cuda.synchronize()
+    ref = T.pack_qkv_int8(q, k, v, P)
+    assert np.array_equal(send.cpu().numpy(), ref)
+    del send
+    # receive buffer: chunks from two distinct shards, alternating by source
+    ref2 = T.pack_qkv_int8(*(bf16_values(rng, (B, H, Ns, d)) for _ in range(3)), P)
+    recv = T.all_to_all([ref, ref2] * (P // 2))[0]
+    got = sa.solattn_unpack_qkv_int8(torch.from_numpy(recv).cuda(), d)
+    torch.cuda.synchronize()
+    for g, r in zip(got, T.unpack_qkv_int8(recv, d)):
+        assert np.array_equal(to_np_bf16(g).view(np.uint32), r.view(np.uint32))
+    del got, recv
+    o = bf16_values(rng, (B, Hp, P * Ns, d))
+    osend = sa.solattn_pack_out_fp8(to_dev(o), P)
+    torch.cuda.synchronize()
+    oref = T.pack_out_fp8(o, P)
+    assert np.array_equal(osend.cpu().numpy(), oref)
+    oref2 = T.pack_out_fp8(bf16_values(rng, (B, Hp, P * Ns, d)), P)
+    orecv = T.all_to_all([oref, oref2] * (P // 2))[0]
+    oback = sa.solattn_unpack_out_fp8(torch.from_numpy(orecv).cuda(), d)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np_bf16(oback).view(np.uint32), T.unpack_out_fp8(orecv, d).view(np.uint32))
