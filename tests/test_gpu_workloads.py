@@ -38,21 +38,34 @@ def workload_inputs(name, seed):
     return _cache[key]
 
 
-def run_workload(name, seed, tau, heads, block_step):
+def oracle_mode(mode):
+    """Binding mode string ("sparse", "topk", "dense", "+video_stats",
+    "+prefix_rows") -> the oracle's mode code."""
+    parts = mode.split("+")
+    code = {"sparse": oracle.SPARSE, "topk": oracle.TOPK, "dense": oracle.DENSE}[parts[0]]
+    for f in parts[1:]:
+        code |= {"video_stats": oracle.VIDEO_STATS, "prefix_rows": oracle.PREFIX_ROWS}[f]
+    return code
+
+
+def run_workload(name, seed, tau, heads, block_step, mode="sparse"):
     import torch
     import block_sparse_video_solattn_amd as sa
     w, q, k, v, (qd, kd, vd) = workload_inputs(name, seed)
     nb = w.nb
-    out, words, _, _ = sa.solattn_forward_debug(qd, kd, vd, None, w.prefix_len, tau, "sparse",
+    out, words, _, _ = sa.solattn_forward_debug(qd, kd, vd, None, w.prefix_len, tau, mode,
                                                 want_scores=False)
     # the production entry point must give the same output as the debug one
-    out2 = sa.solattn_forward(qd, kd, vd, None, w.prefix_len, tau, "sparse")
+    out2 = sa.solattn_forward(qd, kd, vd, None, w.prefix_len, tau, mode)
+    omode = oracle_mode(mode)
+    otau = float(np.float32(tau))   # the value the library receives
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
     gmask = sa.unpack_mask(words, nb)
     n_diff = n_near = 0
     for h in range(w.H):
-        r = oracle.head(q[0, h], k[0, h], v[0, h], w.prefix_len, tau, want_out=False)
+        r = oracle.head(q[0, h], k[0, h], v[0, h], w.prefix_len, otau, mode=omode,
+                        want_out=False)
         nd, nn = mask_compare(gmask, r, 0, h)
         n_diff += nd
         n_near += nn
@@ -62,12 +75,12 @@ def run_workload(name, seed, tau, heads, block_step):
     g = out.float().cpu().numpy()
     worst = 0.0
     for h in heads:
-        r = oracle.head(q[0, h], k[0, h], v[0, h], w.prefix_len, tau,
+        r = oracle.head(q[0, h], k[0, h], v[0, h], w.prefix_len, otau, mode=omode,
                         mask_override=gmask[0, h].astype(np.uint8), qblocks=blocks)
         ab, _ = out_error(g[0, h].astype(np.float64), r["out"], block_rows(blocks, w.N))
         worst = max(worst, ab)
-    print("%s tau=%g: video skip %.4f, mask diffs %d (near-threshold %d), max abs err %.4g"
-          % (name, tau, 1 - gmask[..., pb:].mean(), n_diff, n_near, worst))
+    print("%s %s tau=%g: video skip %.4f, mask diffs %d (near-threshold %d), max abs err %.4g"
+          % (name, mode, tau, 1 - gmask[..., pb:].mean(), n_diff, n_near, worst))
     assert worst <= TOL_BF16_ABS
     return gmask
 
@@ -83,6 +96,24 @@ def test_draft_workload_calibrated_tau():
     m = run_workload("draft", cal["seed"], cal["tau"], heads=(0, 31), block_step=24)
     pb = 8
     assert abs((1 - m[..., pb:].mean()) - 0.90) < 0.01
+
+
+def test_draft_workload_fixed_ratio():
+    # the draft stage's own scheme as the benchmark times it: 10 % of the
+    # video key blocks kept per query block, no pooled terms
+    with open(os.path.join(GOLDEN, "draft_tau.json")) as f:
+        cal = json.load(f)
+    m = run_workload("draft", cal["seed"], 0.1, heads=(0, 31), block_step=24, mode="topk")
+    pb = 8
+    nv = m.shape[-1] - pb
+    assert (m[..., pb:].sum(-1) >= int(np.ceil(np.float64(np.float32(0.1)) * nv))).all()
+
+
+@pytest.mark.parametrize("mode", ["sparse+video_stats", "sparse+prefix_rows"])
+def test_refine_routing_variants(mode):
+    m = run_workload("refine", 3000, 1.25, heads=(0, 31), block_step=16, mode=mode)
+    if mode.endswith("prefix_rows"):
+        assert m[..., :4, :].all()     # prefix query blocks keep every key block
 
 
 def test_long_workload_ragged_tail():
