@@ -25,6 +25,10 @@ are taken:
     the weighted result;
   * the attention consumes the results rounded to the input's element type
     (bf16: nearest, ties to even, straight from the exact value).
+
+tests/test_producer_oracle.py pins each step (a hand-worked row, invariants,
+complex multiplication, brute-force rounding); against the pages, which print
+no formula, the readings above are parity unpinned.
 """
 import numpy as np
 

@@ -6,6 +6,13 @@
  * leg may load it; the product path never does.  It shares no code, header,
  * table or helper with the GPU library.
  *
+ * Every step below is pinned by tests/test_oracle_pins.py against closed
+ * forms, invariants, library routines and hand-worked threshold rows.  The
+ * pages themselves print no formula or numeric example of the operator, so
+ * against the pages the semantics are parity unpinned: the score form, the
+ * standard-deviation convention, the tie rule and the zeroth-order
+ * correction are readings, stated where they are taken.
+ *
  * What it computes (per batch b, head h; Q, K, V are [N][d] row-major):
  *
  *   1. 64-token blocks.  Nb = ceil(N/64), block j holds tokens
