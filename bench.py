@@ -9,7 +9,6 @@ tokens (16x24x42 latent of a 1344x768, 121-frame clip), d=128, bf16, prefix
 """
 import argparse
 import json
-import math
 import os
 import sys
 import time
