@@ -21,8 +21,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
 SEED = 3000
 # extra legs after the headline measurement, in run order
-LEGS = ("mfma_probe", "dense_sweep", "setup", "sp_rank_p8", "qk_producer", "sparsity_90_check",
-        "long_clip")
+LEGS = ("mfma_probe", "dense_sweep", "torch_sdpa", "setup", "sp_rank_p8", "qk_producer",
+        "sparsity_90_check", "long_clip")
 SEED_LONG = 5000
 
 # HBM traffic of one attention dispatch from rocprofv3 counters on this
@@ -373,6 +373,36 @@ def producer_check(sa, stream, tau):
     return res
 
 
+def torch_sdpa_check(q, k, v, ours, stream, sparse_ms, dense_ms):
+    """PyTorch's scaled_dot_product_attention (flash backend only) on the
+    headline inputs: its time, the dense mode's and the sparse call's
+    speedup over it, and its largest difference from the dense mode's
+    output (the same function, dense)."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            ref = F.scaled_dot_product_attention(q, k, v)
+            torch.cuda.synchronize()
+            ms = float(np.median(time_calls(lambda: F.scaled_dot_product_attention(q, k, v), 10,
+                                            stream)))
+    except Exception as e:  # backend missing on this build: report, do not fall back
+        return {"available": False, "reason": str(e)[:160]}
+    B, H, N, d = (int(x) for x in q.shape)
+    import block_sparse_video_solattn_amd as sa
+    sa.solattn_forward(q, k, v, ours, 0, 0.0, "dense")
+    torch.cuda.synchronize()
+    r = {"available": True, "backend": "flash", "ms": round(ms, 3),
+         "tflops": round(4.0 * B * H * N * N * d / (ms * 1e-3) / 1e12, 1),
+         "sparse_speedup": round(ms / sparse_ms, 2),
+         "max_abs_diff_vs_dense_mode": round(float((ours.float() - ref.float()).abs().max()), 5)}
+    if dense_ms:
+        r["dense_mode_speedup"] = round(ms / dense_ms, 2)
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -550,6 +580,12 @@ def main():
             variants[vm] = {"ms": round(vms, 4), "speedup_vs_dense": round(dms / vms, 2),
                             "video_sparsity": round(float(1 - mv[..., pb:].mean()), 4)}
         res["routing_variants"] = variants
+    if "torch_sdpa" in legs:
+        # an outside dense reference on the same inputs: PyTorch's fused
+        # attention, restricted to its flash backend (no fallback to the
+        # unfused math path); reported as unavailable if it cannot run
+        res["torch_sdpa_flash"] = torch_sdpa_check(qd, kd, vd, out, stream, ms_per_step,
+                                                   res.get("dense_ms"))
     if "setup" in legs:
         # routing setup (pooling + scoring/threshold, no attention)
         mw = torch.zeros((B, H, w.nb, (w.nb + 31) // 32), dtype=torch.int32, device="cuda")
