@@ -12,6 +12,10 @@
 //
 // Bound: HBM bandwidth (reads 3 x 64 x d elements per block, writes the value
 // tile once more for bf16).
+//
+// The same file holds produce_pool_kernel, the Q/K producer (QKNorm then
+// partial RoPE) fused with this pass, and the launches of both, which put
+// the (batch, head) slices on grid y in ranges within its limit.
 #include "common.h"
 #include "launch.h"
 #include "producer.h"
