@@ -6,7 +6,7 @@ the built library raises ImportError: there is no CPU fallback.  The input
 generators in ``.inputs`` need no library.
 """
 _BINDING_NAMES = (
-    "BF16", "DENSE", "EXPORTS", "F32", "PREFIX_ROWS", "SPARSE", "TOPK", "VIDEO_STATS",
+    "BF16", "DENSE", "EXPORTS", "F32", "PREFIX_ROWS", "SPARSE", "TAYLOR1", "TOPK", "VIDEO_STATS",
     "SolAttnError", "solattn_attend_ws",
     "solattn_forward", "solattn_forward_debug", "solattn_forward_ws", "solattn_last_error",
     "solattn_pool", "solattn_prepare_ws", "solattn_probe_mfma_bf16", "solattn_route",

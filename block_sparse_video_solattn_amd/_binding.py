@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libsolattn.so")
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
 DENSE, SPARSE, TOPK = 0, 1, 2
 PREFIX_ROWS, VIDEO_STATS = 0x10, 0x20  # routing variant flags, OR-ed into the mode
+TAYLOR1 = 0x40                          # first-order correction of skipped blocks (sparse, bf16)
 F32, BF16 = 0, 1
 
 if not os.path.exists(LIB_PATH):
@@ -115,13 +116,14 @@ def _dtype_code(t) -> int:
 
 
 def _mode_code(mode) -> int:
-    """"dense", "sparse", "topk", optionally followed by "+prefix_rows" and/or
-    "+video_stats" (e.g. "sparse+video_stats"), or the integer code."""
+    """"dense", "sparse", "topk", optionally followed by "+prefix_rows",
+    "+video_stats" and/or "+taylor1" (e.g. "sparse+video_stats"), or the
+    integer code."""
     if isinstance(mode, str):
         parts = mode.split("+")
         code = {"dense": DENSE, "sparse": SPARSE, "topk": TOPK}[parts[0]]
         for f in parts[1:]:
-            code |= {"prefix_rows": PREFIX_ROWS, "video_stats": VIDEO_STATS}[f]
+            code |= {"prefix_rows": PREFIX_ROWS, "video_stats": VIDEO_STATS, "taylor1": TAYLOR1}[f]
         return code
     return int(mode)
 

@@ -51,6 +51,7 @@
 //     one XCD and share its L2 for the K/V tiles they keep.
 #include "common.h"
 #include "launch.h"
+#include "taylor.h"
 #include "route.h"
 
 namespace solattn {
@@ -406,6 +407,66 @@ __device__ __forceinline__ void store_rows(const f32x16 (&oacc)[D / 32][2], cons
     }
 }
 
+// First-order (Taylor) term of the skipped blocks of one query block, added
+// after its exact and pooled tiles, so that the running reference already
+// covers every pooled logit (up to the lazy-rescale slack).  Expanding block
+// j's exact sum around its pooled key to first order adds w_rj c C_j^T q_r to
+// the numerator, w_rj = n_j exp(c q_r.kbar_j) the pooled term's weight and
+// C_j the block's key/value cross-covariance; the denominator's first-order
+// term is zero.  Since the centred keys sum to zero, w_rj c C_j^T q_r =
+// sum_t (w_rj / n_j) c (q_r.k_t - q_r.kbar_j) v_t: a pass over the block's
+// raw key and value tiles with linear weights, no d x d matrix.  Here
+// q_r.kbar_j is the mean over the tile's keys of the S^T products themselves
+// (zero-padded keys past a tail block add zero to the sum; their value rows
+// are zero), and (w_rj / n_j) relative to the row reference is
+// exp2(scale2 * that mean - mref).
+template <int D>
+__device__ __forceinline__ void taylor_first_order(const bf16x8 (&qB)[2][D / 16], const bf16* kp,
+                                                   const bf16* vp, int64_t Nb, int tail,
+                                                   const uint16_t* slist, int n_skip,
+                                                   float scale2, int lane, RowState<D>& rs) {
+    constexpr int KS = D / 16;
+    constexpr int MT = D / 32;
+    const float c = 1.0f / sqrtf((float)D);
+    for (int x = 0; x < n_skip; ++x) {
+        const int64_t j = __builtin_amdgcn_readfirstlane((int)slist[x]);
+        TileRef t;
+        t.ktile = kp + j * (int64_t)D * 64;
+        t.vtile = vp + j * (int64_t)D * 64;
+        t.nvalid = (j == Nb - 1) ? tail : 64;
+        t.bias_off = 0;
+        bf16x8 kA0[KS], kA1[KS];
+        bf16x8 vA0[MT][2], vA1[MT][2];
+        load_k<D>(t, 0, lane, kA0);
+        load_k<D>(t, 1, lane, kA1);
+        load_v<D>(t, 0, lane, vA0);
+        load_v<D>(t, 1, lane, vA1);
+        f32x16 s0[2], s1[2];
+        s_product<D>(kA0, qB, s0);
+        s_product<D>(kA1, qB, s1);
+        float sbar[2], coef[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            float part = 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) part += s0[nt][v] + s1[nt][v];
+            sbar[nt] = sum_across_halves(part) / (float)t.nvalid;
+            coef[nt] = c * __builtin_amdgcn_exp2f(sbar[nt] * scale2 - rs.mref[nt]);
+        }
+        bf16x8 pB[2][2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) pB[nt][v >> 3][v & 7] = to_bf16(coef[nt] * (s0[nt][v] - sbar[nt]));
+        pv_product<D>(vA0, pB, rs);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) pB[nt][v >> 3][v & 7] = to_bf16(coef[nt] * (s1[nt][v] - sbar[nt]));
+        pv_product<D>(vA1, pB, rs);
+    }
+}
+
 }  // namespace
 
 // Rescaling path, for query blocks whose logits grow too far past the
@@ -415,11 +476,12 @@ __device__ __forceinline__ void store_rows(const f32x16 (&oacc)[D / 32][2], cons
 // products of half h+1 are issued before the exp2 work of half h; keys are
 // fetched two halves ahead and values one half ahead, into two register
 // buffers each (buffer = u).
-template <int D>
-__device__ __attribute__((noinline)) void attend_rescaling(
+template <int D, bool TAYLOR>
+__device__ __forceinline__ void rescaling_path(
     const bf16* qp, const bf16* kp, const bf16* vp, const bf16* kbp, const bf16* vbp, bf16* op,
     int64_t N, int64_t Nb, int64_t Nbp, int sparse, int64_t i, int n_kept, uint64_t tile_mask,
-    const float* srow, const uint16_t* klist, const uint16_t* plist) {
+    const float* srow, const uint16_t* klist, const uint16_t* plist, const uint16_t* slist,
+    int n_skip) {
     constexpr int KS = D / 16;
     constexpr int MT = D / 32;
     const int lane = threadIdx.x, half = lane >> 5, l32 = lane & 31;
@@ -493,7 +555,29 @@ __device__ __attribute__((noinline)) void attend_rescaling(
         t0 = t1;
         t1 = t2;
     }
+    if constexpr (TAYLOR) taylor_first_order<D>(qB, kp, vp, Nb, tail, slist, n_skip, scale2, lane, rs);
     store_rows<D>(rs.oacc, rs.lsum, op, i, N, half, l32);
+}
+
+template <int D>
+__device__ __attribute__((noinline)) void attend_rescaling(
+    const bf16* qp, const bf16* kp, const bf16* vp, const bf16* kbp, const bf16* vbp, bf16* op,
+    int64_t N, int64_t Nb, int64_t Nbp, int sparse, int64_t i, int n_kept, uint64_t tile_mask,
+    const float* srow, const uint16_t* klist, const uint16_t* plist) {
+    rescaling_path<D, false>(qp, kp, vp, kbp, vbp, op, N, Nb, Nbp, sparse, i, n_kept, tile_mask,
+                             srow, klist, plist, nullptr, 0);
+}
+
+// Sol-Attn with the first-order (Taylor) term of the skipped blocks: the
+// rescaling path over the exact and pooled tiles, then taylor_first_order.
+template <int D>
+__device__ __attribute__((noinline)) void attend_taylor(
+    const bf16* qp, const bf16* kp, const bf16* vp, const bf16* kbp, const bf16* vbp, bf16* op,
+    int64_t N, int64_t Nb, int64_t Nbp, int64_t i, int n_kept, uint64_t tile_mask,
+    const float* srow, const uint16_t* klist, const uint16_t* plist, const uint16_t* slist,
+    int n_skip) {
+    rescaling_path<D, true>(qp, kp, vp, kbp, vbp, op, N, Nb, Nbp, 1, i, n_kept, tile_mask, srow,
+                            klist, plist, slist, n_skip);
 }
 
 template <int D>
@@ -680,6 +764,64 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
 
     attend_rescaling<D>(qp, kp, vp, kbp, vbp, op, N, Nb, Nbp, a.mode != kDense, i, n_kept, tile_mask,
                         srow, klist, plist);
+}
+
+// Sol-Attn with the first-order (Taylor) correction of the skipped blocks
+// (page "MiniMax 官推背书 Sol Engine：H3 的 10 秒 768p 生成从 414s 压到
+// 14.93s", section "同一项目页上的另一种口径：3.95× 近无损": the skipped
+// blocks' compensation as a Taylor approximation).  An accuracy mode: every
+// skipped block is read and multiplied like an exact tile, so it costs about
+// as much as dense attention.  The routing is the sparse kernel's; the list
+// of skipped blocks comes from the pooled-key biases route_select leaves
+// (finite exactly for the skipped blocks).
+template <int D>
+__global__ __launch_bounds__(64, 1) void attn_bf16_taylor_kernel(AttnArgs a) {
+    extern __shared__ float smem[];
+    const int lane = threadIdx.x;
+    const int64_t N = a.N, Nb = a.Nb, Nbp = a.Nbp;
+    const int64_t w = xcd_remap(blockIdx.x, a.BH * Nb);
+    const int64_t bh = w / Nb, i = w % Nb;
+    // LDS as in attn_bf16_kernel, then the skipped-block list
+    float* srow = smem;
+    const int zero_bias = (int)Nbp, tail_bias = (int)Nbp + 64;
+    uint16_t* klist = reinterpret_cast<uint16_t*>(smem + Nbp + 128);
+    uint16_t* plist = reinterpret_cast<uint16_t*>(smem + Nbp + 128 + (Nb + 15) / 16 * 8);
+    uint16_t* slist = reinterpret_cast<uint16_t*>(smem + Nbp + 128 + (Nb + 15) / 16 * 8 + 32);
+    const bf16* qp = reinterpret_cast<const bf16*>(a.q) + bh * N * D;
+    const bf16* kp = reinterpret_cast<const bf16*>(a.kP) + bh * Nb * D * 64;
+    const bf16* vp = reinterpret_cast<const bf16*>(a.vP) + bh * Nb * D * 64;
+    const bf16* kbp = reinterpret_cast<const bf16*>(a.kbarP) + bh * Nbp * D;
+    const bf16* vbp = reinterpret_cast<const bf16*>(a.vbarP) + bh * Nbp * D;
+    const int tail = (int)(N - (Nb - 1) * 64);
+
+    route_scores<D>(a, bh, i, srow);
+    const RouteResult r = route_select(a, bh, i, srow, klist);
+    srow[zero_bias + lane] = 0.f;
+    srow[tail_bias + lane] = lane < tail ? 0.f : -__builtin_inff();
+    int n_skip = 0;
+    for (int64_t j0 = 0; j0 < Nb; j0 += 64) {
+        const int64_t j = j0 + lane;
+        const bool sk = j < Nb && srow[j] != -__builtin_inff();
+        const uint64_t b = __ballot(sk);
+        if (sk) slist[n_skip + __popcll(b & ((1ull << lane) - 1))] = (uint16_t)j;
+        n_skip += __popcll(b);
+    }
+    if (r.tile_mask >> lane & 1)
+        plist[__popcll(r.tile_mask & ((1ull << lane) - 1))] = (uint16_t)lane;
+    __syncthreads();
+    attend_taylor<D>(qp, kp, vp, kbp, vbp, reinterpret_cast<bf16*>(a.out) + bh * N * D, N, Nb, Nbp,
+                     i, r.n_kept, r.tile_mask, srow, klist, plist, slist, n_skip);
+}
+
+hipError_t launch_attn_bf16_taylor(const AttnArgs& a, hipStream_t s) {
+    const size_t lds = sizeof(float) * (a.Nbp + 128 + (a.Nb + 15) / 16 * 8 + 32) +
+                       sizeof(uint16_t) * ((a.Nb + 15) / 16 * 16);
+    const dim3 grid((unsigned)(a.BH * a.Nb));
+    if (a.d == 128)
+        hipLaunchKernelGGL((attn_bf16_taylor_kernel<128>), grid, dim3(64), lds, s, a);
+    else
+        hipLaunchKernelGGL((attn_bf16_taylor_kernel<64>), grid, dim3(64), lds, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {

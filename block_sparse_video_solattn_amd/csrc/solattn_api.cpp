@@ -17,6 +17,7 @@
 #include "../../include/solattn_transport.h"
 #include "launch.h"
 #include "producer.h"
+#include "taylor.h"
 
 using namespace solattn;
 
@@ -65,8 +66,10 @@ int validate(const void* q, const void* k, const void* v, const void* out, bool 
     const int base = mode & SOLATTN_MODE_MASK, flags = mode & ~SOLATTN_MODE_MASK;
     if (base != SOLATTN_DENSE && base != SOLATTN_SPARSE && base != SOLATTN_TOPK)
         return fail(SOLATTN_EINVAL, "unknown mode %d", mode);
-    if (flags & ~(SOLATTN_PREFIX_ROWS | SOLATTN_VIDEO_STATS))
+    if (flags & ~(SOLATTN_PREFIX_ROWS | SOLATTN_VIDEO_STATS | SOLATTN_TAYLOR1))
         return fail(SOLATTN_EINVAL, "unknown mode flags 0x%x", flags);
+    if ((flags & SOLATTN_TAYLOR1) && base != SOLATTN_SPARSE)
+        return fail(SOLATTN_EINVAL, "SOLATTN_TAYLOR1 needs SPARSE");
     if ((flags & SOLATTN_PREFIX_ROWS) && base == SOLATTN_DENSE)
         return fail(SOLATTN_EINVAL, "SOLATTN_PREFIX_ROWS needs SPARSE or TOPK");
     if ((flags & SOLATTN_VIDEO_STATS) && base != SOLATTN_SPARSE)
@@ -76,6 +79,8 @@ int validate(const void* q, const void* k, const void* v, const void* out, bool 
                     (double)tau);
     if (dtype != SOLATTN_F32 && dtype != SOLATTN_BF16)
         return fail(SOLATTN_EINVAL, "unknown dtype %d", dtype);
+    if ((flags & SOLATTN_TAYLOR1) && dtype != SOLATTN_BF16)
+        return fail(SOLATTN_EUNSUPPORTED, "SOLATTN_TAYLOR1 is built for bf16 only");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (out && !aligned16(out)))
         return fail(SOLATTN_EINVAL, "tensor pointers must be 16-byte aligned");
     if (N > kMaxN)
@@ -241,8 +246,10 @@ int run_attend(const void* q, const void* k, const void* v, void* out, int64_t B
         int64_t kk = base == SOLATTN_TOPK ? (int64_t)std::ceil((double)tau * (double)nv) : 0;
         a.topk = kk > nv ? nv : kk;
     }
-    hipError_t e = route_only ? launch_route(a, s)
-                              : dtype == kBF16 ? launch_attn_bf16(a, s) : launch_attn_f32(a, s);
+    hipError_t e = route_only                  ? launch_route(a, s)
+                   : (mode & SOLATTN_TAYLOR1) ? launch_attn_bf16_taylor(a, s)
+                   : dtype == kBF16           ? launch_attn_bf16(a, s)
+                                              : launch_attn_f32(a, s);
     if (e != hipSuccess) return hip_fail(e, route_only ? "route kernel launch" : "attention kernel launch");
     return SOLATTN_OK;
 }

@@ -94,6 +94,19 @@ extern "C" {
 #define SOLATTN_MODE_MASK 0x0f
 #define SOLATTN_PREFIX_ROWS 0x10
 #define SOLATTN_VIDEO_STATS 0x20
+/*
+ * SOLATTN_TAYLOR1 (SPARSE, bf16; may be combined with the two flags above):
+ * the skipped blocks' pooled term taken to first order (page "MiniMax 官推
+ * 背书 Sol Engine：H3 的 10 秒 768p 生成从 414s 压到 14.93s", section "同一项目
+ * 页上的另一种口径：3.95× 近无损", which calls the compensation a Taylor
+ * approximation).  Skipped block j's value vbar_j becomes, for query row r,
+ * vbar_j + c C_j^T q_r with C_j = (1/n_j) sum_t (k_t - kbar_j)(v_t - vbar_j)^T,
+ * c = 1/sqrt(d); its weight n_j exp(c q_r.kbar_j) and the denominator are
+ * unchanged (their first-order term is zero).  An accuracy mode: every
+ * skipped block's key and value tiles are read and multiplied, about the
+ * cost of dense attention.  With fp32 data: SOLATTN_EUNSUPPORTED.
+ */
+#define SOLATTN_TAYLOR1 0x40
 
 /* dtype */
 #define SOLATTN_F32 0
