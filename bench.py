@@ -21,8 +21,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
 SEED = 3000
 # extra legs after the headline measurement, in run order
-LEGS = ("mfma_probe", "dense_sweep", "torch_sdpa", "setup", "sp_rank_p8", "qk_producer",
-        "sparsity_90_check", "long_clip")
+LEGS = ("mfma_probe", "dense_sweep", "torch_sdpa", "taylor1", "setup", "sp_rank_p8",
+        "qk_producer", "sparsity_90_check", "long_clip")
 SEED_LONG = 5000
 
 # HBM traffic of one attention dispatch from rocprofv3 counters on this
@@ -32,11 +32,11 @@ SEED_LONG = 5000
 # they were measured on; after any change to those sources the traffic is
 # reported as null until the counters are taken again.
 ATTN_COUNTERS = {
-    "sources_sha256": "5f45acd437e391df1b2fa4a67710bf831ac2530466c05ac28f9fe4f958684f3e",
-    "fetch_kib": 737909.7, "fetch_scale": 2.0,
-    "write_kib": 131083.6, "write_scale": 1.0,
+    "sources_sha256": "a992875533f2ac2545d10946778c6f0d9d83b7abc3eb3bf0ed3a02fd2f1f60b0",
+    "fetch_kib": 738077.3, "fetch_scale": 2.0,
+    "write_kib": 131079.6, "write_scale": 1.0,
 }
-ATTN_SOURCES = ("attn_bf16.hip", "route.h", "common.h", "launch.h")
+ATTN_SOURCES = ("attn_bf16.hip", "route.h", "common.h", "launch.h", "taylor.h")
 
 
 def attn_sources_sha256():
@@ -403,6 +403,33 @@ def torch_sdpa_check(q, k, v, ours, stream, sparse_ms, dense_ms):
     return r
 
 
+def taylor_check(sa, stream, q, k, v, prefix_len, tau, ws):
+    """The first-order (Taylor) accuracy mode on the headline inputs: its
+    time beside the zeroth-order call and the dense mode, and how far each
+    sparse output lies from dense attention (max and mean absolute
+    difference over all heads and rows)."""
+    import numpy as np
+    import torch
+    outs = {}
+    ms = {}
+    for name, mode, t in (("sparse", "sparse", tau), ("taylor1", "sparse+taylor1", tau),
+                          ("dense", "dense", 0.0)):
+        o = torch.empty_like(q)
+
+        def call(mode=mode, t=t, o=o):
+            sa.solattn_forward_ws(q, k, v, o, prefix_len, t, mode, ws)
+        call()
+        ms[name] = float(np.median(time_calls(call, 10, stream)))
+        outs[name] = o
+    torch.cuda.synchronize()
+    res = {"tau": tau, "ms": {n: round(x, 4) for n, x in ms.items()}}
+    for name in ("sparse", "taylor1"):
+        d = (outs[name].float() - outs["dense"].float()).abs()
+        res[name + "_vs_dense"] = {"max_abs": round(float(d.max()), 5),
+                                   "mean_abs": round(float(d.mean()), 6)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -586,6 +613,8 @@ def main():
         # unfused math path); reported as unavailable if it cannot run
         res["torch_sdpa_flash"] = torch_sdpa_check(qd, kd, vd, out, stream, ms_per_step,
                                                    res.get("dense_ms"))
+    if "taylor1" in legs:
+        res["taylor1"] = taylor_check(sa, stream, qd, kd, vd, w.prefix_len, tau, ws)
     if "setup" in legs:
         # routing setup (pooling + scoring/threshold, no attention)
         mw = torch.zeros((B, H, w.nb, (w.nb + 31) // 32), dtype=torch.int32, device="cuda")
