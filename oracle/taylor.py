@@ -49,19 +49,21 @@ def block_cov(k: np.ndarray, v: np.ndarray, lo: int, hi: int) -> np.ndarray:
 
 
 def head(q, k, v, prefix_len: int, tau: float, order: int = 1,
-         mask_override: Optional[np.ndarray] = None, rows: Optional[np.ndarray] = None) -> dict:
+         mask_override: Optional[np.ndarray] = None, rows: Optional[np.ndarray] = None,
+         mode: int = oracle.SPARSE) -> dict:
     """One slice: q, k, v [N, d].  Returns {"out": [len(rows), d], "mask"}.
 
     order 0: exact kept blocks plus the pooled zeroth-order term of every
     skipped block (the default operator); order 1: the skipped blocks'
     values also carry c C_j^T q_r.  mask_override replaces the routing
-    (several masks are correct where a score sits on its threshold)."""
+    (several masks are correct where a score sits on its threshold); mode
+    is the C oracle's routing mode (SPARSE with its variant flags)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     N, d = q.shape
     nb = (N + BLOCK - 1) // BLOCK
-    r = oracle.head(q, k, v, prefix_len, tau, want_out=False)
+    r = oracle.head(q, k, v, prefix_len, tau, mode=mode, want_out=False)
     mask = r["mask"].astype(bool) if mask_override is None else np.asarray(mask_override, bool)
     c = 1.0 / np.sqrt(d)
     rows = np.arange(N) if rows is None else np.asarray(rows)

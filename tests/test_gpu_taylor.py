@@ -100,3 +100,17 @@ def test_refine_shape_sampled():
         r = OT.head(q[0, hi], k[0, hi], v[0, hi], w.prefix_len, 1.25, order=1,
                     mask_override=gmask[0, hi], rows=rows)
         assert np.abs(g[0, hi, rows] - r["out"]).max() <= TOL_BF16_ABS
+
+
+@pytest.mark.parametrize("flags,omode", [("+video_stats", oracle.SPARSE | oracle.VIDEO_STATS),
+                                         ("+prefix_rows", oracle.SPARSE | oracle.PREFIX_ROWS)])
+def test_taylor_with_routing_variants(flags, omode):
+    q, k, v = inputs.custom(1, 2, 1500, 128, "bf16", prefix_len=192, seed=93, kind="field",
+                            grid=(2, 24, 28))
+    g, gmask = _run(q, k, v, 192, 1.0, mode="sparse" + flags + "+taylor1")
+    for h in range(2):
+        ro = oracle.head(q[0, h], k[0, h], v[0, h], 192, 1.0, mode=omode, want_out=False)
+        mask_compare(gmask, ro, 0, h)
+        r = OT.head(q[0, h], k[0, h], v[0, h], 192, 1.0, order=1, mask_override=gmask[0, h],
+                    mode=omode)
+        assert np.abs(g[0, h] - r["out"]).max() <= TOL_BF16_ABS
