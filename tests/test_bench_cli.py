@@ -28,5 +28,6 @@ def test_unknown_leg_is_rejected():
 def test_legs_listed_in_help():
     r = _run("--help")
     assert r.returncode == 0
-    for leg in ("mfma_probe", "dense_sweep", "torch_sdpa", "qk_producer", "long_clip"):
-        assert leg in r.stdout
+    text = "".join(r.stdout.split())      # argparse wraps the list where it likes
+    for leg in ("mfma_probe", "dense_sweep", "torch_sdpa", "taylor1", "qk_producer", "long_clip"):
+        assert leg in text
