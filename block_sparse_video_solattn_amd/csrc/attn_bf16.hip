@@ -428,22 +428,35 @@ __device__ __forceinline__ void taylor_first_order(const bf16x8 (&qB)[2][D / 16]
     constexpr int KS = D / 16;
     constexpr int MT = D / 32;
     const float c = 1.0f / sqrtf((float)D);
-    for (int x = 0; x < n_skip; ++x) {
+    if (n_skip == 0) return;
+    auto tile = [&](int x) -> TileRef {
         const int64_t j = __builtin_amdgcn_readfirstlane((int)slist[x]);
         TileRef t;
         t.ktile = kp + j * (int64_t)D * 64;
         t.vtile = vp + j * (int64_t)D * 64;
         t.nvalid = (j == Nb - 1) ? tail : 64;
         t.bias_off = 0;
-        bf16x8 kA0[KS], kA1[KS];
-        bf16x8 vA0[MT][2], vA1[MT][2];
-        load_k<D>(t, 0, lane, kA0);
-        load_k<D>(t, 1, lane, kA1);
-        load_v<D>(t, 0, lane, vA0);
-        load_v<D>(t, 1, lane, vA1);
+        return t;
+    };
+    // software pipeline in the operand registers themselves: the keys of
+    // block x+1 are requested once the S^T products of block x have read
+    // theirs, the values of block x+1 once its PV products have
+    bf16x8 kA0[KS], kA1[KS];
+    bf16x8 vA0[MT][2], vA1[MT][2];
+    TileRef t = tile(0);
+    load_k<D>(t, 0, lane, kA0);
+    load_k<D>(t, 1, lane, kA1);
+    load_v<D>(t, 0, lane, vA0);
+    load_v<D>(t, 1, lane, vA1);
+    for (int x = 0; x < n_skip; ++x) {
+        const TileRef tn = x + 1 < n_skip ? tile(x + 1) : t;
         f32x16 s0[2], s1[2];
         s_product<D>(kA0, qB, s0);
         s_product<D>(kA1, qB, s1);
+        if (x + 1 < n_skip) {
+            load_k<D>(tn, 0, lane, kA0);
+            load_k<D>(tn, 1, lane, kA1);
+        }
         float sbar[2], coef[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
@@ -464,6 +477,11 @@ __device__ __forceinline__ void taylor_first_order(const bf16x8 (&qB)[2][D / 16]
 #pragma unroll
             for (int v = 0; v < 16; ++v) pB[nt][v >> 3][v & 7] = to_bf16(coef[nt] * (s1[nt][v] - sbar[nt]));
         pv_product<D>(vA1, pB, rs);
+        if (x + 1 < n_skip) {
+            load_v<D>(tn, 0, lane, vA0);
+            load_v<D>(tn, 1, lane, vA1);
+        }
+        t = tn;
     }
 }
 
