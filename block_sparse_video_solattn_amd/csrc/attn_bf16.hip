@@ -49,6 +49,10 @@
 //     v_permlane32_swap between the lane halves;
 //   * workgroups are remapped so that the query blocks of one head run on
 //     one XCD and share its L2 for the K/V tiles they keep.
+// The file also holds attn_bf16_taylor_kernel, the first-order (Taylor)
+// accuracy mode: the same routing, the rescaling path over the exact and
+// pooled tiles, then a pass over every skipped block (see
+// taylor_first_order).
 #include "common.h"
 #include "launch.h"
 #include "taylor.h"
