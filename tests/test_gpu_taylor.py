@@ -38,6 +38,8 @@ def _run(q, k, v, prefix, tau, mode="sparse+taylor1"):
     (1, 2, 1000, 128, 64, 1.0, "iid_qk_offset"),    # ragged tail of 40 keys
     (2, 1, 64 * 9 + 5, 64, 0, 0.5, "iid_qk_offset"),  # tail of 5, B > 1, d = 64
     (1, 2, 2000, 128, 128, 1.25, "field"),
+    (1, 1, 700, 128, 0, float("inf"), "iid_qk_offset"),     # every block skipped
+    (1, 1, 700, 64, 0, float("-inf"), "iid_qk_offset"),     # none skipped: dense
 ])
 def test_taylor_matches_oracle(B, H, N, d, prefix, tau, kind):
     grid = (2, 24, 40) if kind == "field" else None
