@@ -137,7 +137,15 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _on_gpu(t, name):
+    """Every tensor handed to the library must live in GPU memory: a host
+    pointer reaching a kernel would fault the device."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError("%s must be a GPU tensor (got device %s)" % (name, getattr(t, "device", "?")))
+
+
 def _shape(q):
+    _on_gpu(q, "q")
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     for t in (q,):
@@ -150,8 +158,23 @@ def _check_like(q, *ts):
     for t in ts:
         if t is None:
             continue
+        _on_gpu(t, "k, v and out")
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
             raise ValueError("q, k, v, out must share shape, dtype, device and be contiguous")
+
+
+def _same_device(q, t, name):
+    """Workspaces, exports and tables: a GPU tensor on q's device, contiguous."""
+    if t is None:
+        return
+    _on_gpu(t, name)
+    if t.device != q.device or not t.is_contiguous():
+        raise ValueError("%s must be contiguous and on %s" % (name, q.device))
+
+
+def _ws_bytes(q, ws):
+    _same_device(q, ws, "ws")
+    return ws.numel() * ws.element_size()
 
 
 def solattn_workspace_bytes(B: int, H: int, N: int, d: int, dtype) -> int:
@@ -176,7 +199,7 @@ def solattn_forward_ws(q, k, v, out, prefix_len, tau, mode, ws, stream=None):
     _check_like(q, k, v, out)
     _check(_lib.solattn_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, prefix_len,
                                    float(tau), _mode_code(mode), _dtype_code(q), _ptr(ws),
-                                   ws.numel() * ws.element_size(), _stream(stream)))
+                                   _ws_bytes(q, ws), _stream(stream)))
     return out
 
 
@@ -184,7 +207,7 @@ def solattn_prepare_ws(q, k, v, mode, ws, stream=None):
     B, H, N, d = _shape(q)
     _check_like(q, k, v)
     _check(_lib.solattn_prepare_ws(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, _mode_code(mode),
-                                   _dtype_code(q), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _dtype_code(q), _ptr(ws), _ws_bytes(q, ws),
                                    _stream(stream)))
 
 
@@ -193,7 +216,7 @@ def solattn_attend_ws(q, k, v, out, prefix_len, tau, mode, ws, stream=None):
     _check_like(q, k, v, out)
     _check(_lib.solattn_attend_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, prefix_len,
                                   float(tau), _mode_code(mode), _dtype_code(q), _ptr(ws),
-                                  ws.numel() * ws.element_size(), _stream(stream)))
+                                  _ws_bytes(q, ws), _stream(stream)))
     return out
 
 
@@ -241,6 +264,8 @@ def solattn_route(q, k, v, prefix_len: int, tau: float, stream=None, want_scores
         scores = torch.full((B, H, nb, nb), float("nan"), dtype=torch.float32, device=q.device)
     if thr is None:
         thr = torch.full((B, H, nb), float("nan"), dtype=torch.float32, device=q.device)
+    for t, name in ((mask, "mask"), (scores, "scores"), (thr, "thr")):
+        _same_device(q, t, name)
     _check(_lib.solattn_route(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, prefix_len, float(tau),
                               _dtype_code(q), _ptr(mask), _ptr(scores), _ptr(thr), _stream(stream)))
     return mask, scores, thr
@@ -249,6 +274,7 @@ def solattn_route(q, k, v, prefix_len: int, tau: float, stream=None, want_scores
 def solattn_probe_mfma_bf16(sink, waves: int, iters: int, stream=None):
     """Enqueue the bf16 MFMA peak probe (waves * iters * 16 * 32768 FLOP);
     sink: float32 device tensor of at least waves * 64 elements."""
+    _on_gpu(sink, "sink")
     if sink.numel() < waves * 64:
         raise ValueError("sink needs waves * 64 floats")
     _check(_lib.solattn_probe_mfma_bf16(_ptr(sink), int(waves), int(iters), _stream(stream)))
@@ -279,6 +305,7 @@ def solattn_transport_record_bytes(d: int) -> int:
 
 def _bf16_4d(t, name):
     import torch
+    _on_gpu(t, name)
     if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
         raise ValueError("%s must be a contiguous 4-d bfloat16 tensor" % name)
     return tuple(t.shape)
@@ -294,6 +321,7 @@ def solattn_pack_qkv_int8(q, k, v, P: int, send=None, stream=None):
     rec = solattn_transport_record_bytes(d)
     if send is None:
         send = torch.empty((P, B, H // max(P, 1), Ns, 3, rec), dtype=torch.uint8, device=q.device)
+    _same_device(q, send, "send")
     _check(_lib.solattn_pack_qkv_int8(_ptr(q), _ptr(k), _ptr(v), B, H, Ns, d, int(P), _ptr(send),
                                       _stream(stream)))
     return send
@@ -302,11 +330,14 @@ def solattn_pack_qkv_int8(q, k, v, P: int, send=None, stream=None):
 def solattn_unpack_qkv_int8(recv, d: int, q=None, k=None, v=None, stream=None):
     """Received records [P][B][Hp][Ns][3][rec] -> q, k, v [B][Hp][P*Ns][d] bf16."""
     import torch
+    _on_gpu(recv, "recv")
     P, B, Hp, Ns = (int(x) for x in recv.shape[:4])
     shape = (B, Hp, P * Ns, d)
     q = torch.empty(shape, dtype=torch.bfloat16, device=recv.device) if q is None else q
     k = torch.empty(shape, dtype=torch.bfloat16, device=recv.device) if k is None else k
     v = torch.empty(shape, dtype=torch.bfloat16, device=recv.device) if v is None else v
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _same_device(recv, t, name)
     _check(_lib.solattn_unpack_qkv_int8(_ptr(recv), B, Hp, Ns, int(d), P, _ptr(q), _ptr(k), _ptr(v),
                                         _stream(stream)))
     return q, k, v
@@ -323,6 +354,7 @@ def solattn_pack_out_fp8(o, P: int, send=None, stream=None):
     if send is None:
         send = torch.empty((P, B, Hp, Ns, solattn_transport_record_bytes(d)), dtype=torch.uint8,
                            device=o.device)
+    _same_device(o, send, "send")
     _check(_lib.solattn_pack_out_fp8(_ptr(o), B, Hp, Ns, d, int(P), _ptr(send), _stream(stream)))
     return send
 
@@ -330,9 +362,11 @@ def solattn_pack_out_fp8(o, P: int, send=None, stream=None):
 def solattn_unpack_out_fp8(recv, d: int, o=None, stream=None):
     """Received records [P][B][Hp][Ns][rec] -> o [B][P*Hp][Ns][d] bf16."""
     import torch
+    _on_gpu(recv, "recv")
     P, B, Hp, Ns = (int(x) for x in recv.shape[:4])
     if o is None:
         o = torch.empty((B, P * Hp, Ns, d), dtype=torch.bfloat16, device=recv.device)
+    _same_device(recv, o, "o")
     _check(_lib.solattn_unpack_out_fp8(_ptr(recv), B, Hp, Ns, int(d), P, _ptr(o), _stream(stream)))
     return o
 
@@ -342,6 +376,7 @@ def _f32_vec(t, n, name):
     import torch
     if t is None:
         return None
+    _on_gpu(t, name)
     if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
         raise ValueError("%s must be a contiguous float32 tensor of %d elements" % (name, n))
     return t
@@ -354,6 +389,10 @@ def _producer_ptrs(q, gamma_q, gamma_k, rope_dim, rope_cos, rope_sin):
     if rope_dim > 0:
         _f32_vec(rope_cos, N * (rope_dim // 2), "rope_cos")
         _f32_vec(rope_sin, N * (rope_dim // 2), "rope_sin")
+    for t, name in ((gamma_q, "gamma_q"), (gamma_k, "gamma_k"), (rope_cos, "rope_cos"),
+                    (rope_sin, "rope_sin")):
+        if t is not None and (rope_dim > 0 or name.startswith("gamma")):
+            _same_device(q, t, name)
     return B, H, N, d
 
 
@@ -385,5 +424,5 @@ def solattn_prepare_qknorm_rope_ws(q, k, v, gamma_q, gamma_k, eps: float, rope_d
     _check(_lib.solattn_prepare_qknorm_rope_ws(
         _ptr(q), _ptr(k), _ptr(v), _ptr(gamma_q), _ptr(gamma_k), float(eps), int(rope_dim),
         _ptr(rope_cos), _ptr(rope_sin), _ptr(q_out), _ptr(k_out), B, H, N, d, _mode_code(mode),
-        _dtype_code(q), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+        _dtype_code(q), _ptr(ws), _ws_bytes(q, ws), _stream(stream)))
     return q_out, k_out

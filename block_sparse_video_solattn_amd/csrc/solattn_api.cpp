@@ -1,5 +1,6 @@
-// Host side of the Sol-Attn C ABI: argument checks, the per-device workspace
-// cache, and the launch sequence (pool, then fused route + attention).
+// Host side of the Sol-Attn C ABI: argument checks, the internal workspaces
+// (one per device and stream), and the launch sequence (pool, then fused
+// route + attention).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -132,41 +133,92 @@ int check_buffers(std::initializer_list<const void*> in, size_t in_bytes,
     return SOLATTN_OK;
 }
 
-struct DeviceWs {
-    void* ptr = nullptr;
-    size_t bytes = 0;
+// Every pointer the kernels will dereference must be GPU memory: a host
+// pointer reaching a kernel faults the device.  Checked last, after the
+// pure host-side checks, with one runtime query per distinct pointer
+// (NULL entries are skipped; they were checked above where they matter).
+int check_device_ptrs(std::initializer_list<const void*> ptrs) {
+    const void* seen[16];
+    int n = 0;
+    for (const void* p : ptrs) {
+        if (!p) continue;
+        bool dup = false;
+        for (int i = 0; i < n; ++i) dup = dup || seen[i] == p;
+        if (dup) continue;
+        if (n < 16) seen[n++] = p;
+        hipPointerAttribute_t attr;
+        const hipError_t e = hipPointerGetAttributes(&attr, p);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(SOLATTN_EINVAL, "pointer %p is not memory HIP knows (%s): pass device memory",
+                        p, hipGetErrorString(e));
+        }
+        if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged &&
+            attr.type != hipMemoryTypeUnified)
+            return fail(SOLATTN_EINVAL, "pointer %p is not device memory (memory type %d)", p,
+                        (int)attr.type);
+    }
+    return SOLATTN_OK;
+}
+
+// Internal workspaces of the plain entry points: one buffer per (device,
+// stream), so that plain calls on different streams never share memory.
+// A buffer handed out is never freed while the library is loaded: when a
+// slot must grow, the old buffer moves to a retired list (work already
+// enqueued, or a host thread that holds the pointer but has not launched
+// yet, may still use it).  Growth is at least 2x, so the retired buffers of
+// a slot never total more than its current one.  Everything is held until
+// the process ends.
+struct WsSlot {
+    int dev;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
 };
 std::mutex g_ws_mutex;
-std::vector<DeviceWs> g_ws;
+std::vector<WsSlot> g_ws;
+std::vector<void*> g_ws_retired;
 
-// Internal workspace of the current device, grown on demand.  Growing
-// synchronises the device first so no launch still reads the old buffer.
-int internal_ws(size_t need, void** out) {
+// The plain entry points may allocate, so they cannot be recorded into a
+// graph (a captured call would also bake in a buffer a later growth
+// retires).  Checked before any other runtime call of such an entry point.
+int reject_capture(hipStream_t stream) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cap != hipStreamCaptureStatusNone)
+        return fail(SOLATTN_EUNSUPPORTED,
+                    "the stream is being captured: the entry points without a workspace argument "
+                    "may allocate; use the _ws entry points under capture");
+    return SOLATTN_OK;
+}
+
+int internal_ws(size_t need, hipStream_t stream, void** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-    DeviceWs& w = g_ws[dev];
-    if (w.bytes < need) {
-        if (w.ptr) {
-            e = hipDeviceSynchronize();
-            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-            e = hipFree(w.ptr);
-            if (e != hipSuccess) return hip_fail(e, "hipFree");
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        e = hipMalloc(&w.ptr, need);
+    WsSlot* w = nullptr;
+    for (WsSlot& x : g_ws)
+        if (x.dev == dev && x.stream == stream) w = &x;
+    if (!w) {
+        g_ws.push_back(WsSlot{dev, stream, nullptr, 0});
+        w = &g_ws.back();
+    }
+    if (w->bytes < need) {
+        const size_t grow = need > 2 * w->bytes ? need : 2 * w->bytes;
+        void* p = nullptr;
+        e = hipMalloc(&p, grow);
         if (e != hipSuccess) {
-            w.ptr = nullptr;
             (void)hipGetLastError();
-            return fail(SOLATTN_ENOMEM, "workspace allocation of %zu bytes failed: %s", need,
+            return fail(SOLATTN_ENOMEM, "workspace allocation of %zu bytes failed: %s", grow,
                         hipGetErrorString(e));
         }
-        w.bytes = need;
+        if (w->ptr) g_ws_retired.push_back(w->ptr);
+        w->ptr = p;
+        w->bytes = grow;
     }
-    *out = w.ptr;
+    *out = w->ptr;
     return SOLATTN_OK;
 }
 
@@ -328,6 +380,8 @@ int solattn_qknorm_rope(const void* q, const void* k, const float* gamma_q,
     if ((rc = check_producer(q, k, nullptr, gamma_q, gamma_k, eps, rope_dim, rope_cos, rope_sin,
                              q_out, k_out, false, B, H, N, d, dtype, &pa)))
         return rc;
+    if ((rc = check_device_ptrs({q, k, q_out, k_out, gamma_q, gamma_k, pa.rope_cos, pa.rope_sin})))
+        return rc;
     PoolArgs p = {};
     p.q = q;
     p.k = k;
@@ -356,6 +410,9 @@ int solattn_prepare_qknorm_rope_ws(const void* q, const void* k, const void* v,
     if ((rc = check_producer(q, k, v, gamma_q, gamma_k, eps, rope_dim, rope_cos, rope_sin, q_out,
                              k_out, dtype == SOLATTN_BF16, B, H, N, d, dtype, &pa)))
         return rc;
+    if ((rc = check_device_ptrs({q, k, v, q_out, k_out, gamma_q, gamma_k, pa.rope_cos, pa.rope_sin,
+                                 ws})))
+        return rc;
     const PoolArgs p = pool_args(q, k, v, B, H, N, d, mode, dtype, ws, true);
     hipError_t e = launch_produce_pool(p, pa, B * H, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "producer kernel launch");
@@ -373,6 +430,7 @@ int solattn_forward_ws(const void* q, const void* k, const void* v, void* out, i
     int rc = validate(q, k, v, out, true, B, H, N, d, prefix_len, tau, mode, dtype);
     if (rc) return rc;
     if ((rc = check_ws(ws, ws_bytes, B, H, N, d, dtype))) return rc;
+    if ((rc = check_device_ptrs({q, k, v, out, ws}))) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = run_prepare(q, k, v, B, H, N, d, mode, dtype, ws, s, true))) return rc;
     return run_attend(q, k, v, out, B, H, N, d, prefix_len, tau, mode, dtype, ws, s, nullptr,
@@ -384,9 +442,11 @@ int solattn_forward(const void* q, const void* k, const void* v, void* out, int6
                     void* stream) {
     int rc = validate(q, k, v, out, true, B, H, N, d, prefix_len, tau, mode, dtype);
     if (rc) return rc;
+    if ((rc = reject_capture(static_cast<hipStream_t>(stream)))) return rc;
+    if ((rc = check_device_ptrs({q, k, v, out}))) return rc;
     void* ws = nullptr;
     const size_t need = ws_layout(B, H, N, d, dtype).total;
-    if ((rc = internal_ws(need, &ws))) return rc;
+    if ((rc = internal_ws(need, static_cast<hipStream_t>(stream), &ws))) return rc;
     return solattn_forward_ws(q, k, v, out, B, H, N, d, prefix_len, tau, mode, dtype, ws, need,
                               stream);
 }
@@ -397,6 +457,7 @@ int solattn_prepare_ws(const void* q, const void* k, const void* v, int64_t B, i
     int rc = validate(q, k, v, nullptr, false, B, H, N, d, 0, 0.f, mode, dtype);
     if (rc) return rc;
     if ((rc = check_ws(ws, ws_bytes, B, H, N, d, dtype))) return rc;
+    if ((rc = check_device_ptrs({q, k, v, ws}))) return rc;
     return run_prepare(q, k, v, B, H, N, d, mode, dtype, ws, static_cast<hipStream_t>(stream), true);
 }
 
@@ -408,6 +469,7 @@ int solattn_attend_ws(const void* q, const void* k, const void* v, void* out, in
                       dtype == SOLATTN_BF16);
     if (rc) return rc;
     if ((rc = check_ws(ws, ws_bytes, B, H, N, d, dtype))) return rc;
+    if ((rc = check_device_ptrs({q, k, v, out, ws}))) return rc;
     return run_attend(q, k, v, out, B, H, N, d, prefix_len, tau, mode, dtype, ws,
                       static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, 0);
 }
@@ -418,9 +480,11 @@ int solattn_forward_debug(const void* q, const void* k, const void* v, void* out
                           float* thr_out, void* stream) {
     int rc = validate(q, k, v, out, true, B, H, N, d, prefix_len, tau, mode, dtype);
     if (rc) return rc;
+    if ((rc = reject_capture(static_cast<hipStream_t>(stream)))) return rc;
+    if ((rc = check_device_ptrs({q, k, v, out, mask_out, score_out, thr_out}))) return rc;
     void* ws = nullptr;
-    if ((rc = internal_ws(ws_layout(B, H, N, d, dtype).total, &ws))) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = internal_ws(ws_layout(B, H, N, d, dtype).total, s, &ws))) return rc;
     if ((rc = run_prepare(q, k, v, B, H, N, d, mode, dtype, ws, s, true))) return rc;
     return run_attend(q, k, v, out, B, H, N, d, prefix_len, tau, mode, dtype, ws, s, mask_out,
                       score_out, thr_out, 0);
@@ -431,10 +495,12 @@ int solattn_pool(const void* q, const void* k, const void* v, float* qbar, float
                  void* stream) {
     int rc = validate(q, k, v, nullptr, false, B, H, N, d, 0, 0.f, SOLATTN_SPARSE, dtype);
     if (rc) return rc;
+    if ((rc = reject_capture(static_cast<hipStream_t>(stream)))) return rc;
+    if ((rc = check_device_ptrs({q, k, v, qbar, kbar, vbar}))) return rc;
     void* ws = nullptr;
     const WsLayout L = ws_layout(B, H, N, d, dtype);
-    if ((rc = internal_ws(L.total, &ws))) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = internal_ws(L.total, s, &ws))) return rc;
     if ((rc = run_prepare(q, k, v, B, H, N, d, SOLATTN_SPARSE, dtype, ws, s, false))) return rc;
     const size_t bytes = sizeof(float) * B * H * ((N + 63) / 64) * d;
     const struct { float* dst; size_t off; } outs[3] = {{qbar, L.qbar}, {kbar, L.kbar}, {vbar, L.vbar}};
@@ -451,9 +517,11 @@ int solattn_route(const void* q, const void* k, const void* v, int64_t B, int64_
                   float* score_out, float* thr_out, void* stream) {
     int rc = validate(q, k, v, nullptr, false, B, H, N, d, prefix_len, tau, SOLATTN_SPARSE, dtype);
     if (rc) return rc;
+    if ((rc = reject_capture(static_cast<hipStream_t>(stream)))) return rc;
+    if ((rc = check_device_ptrs({q, k, v, mask_out, score_out, thr_out}))) return rc;
     void* ws = nullptr;
-    if ((rc = internal_ws(ws_layout(B, H, N, d, dtype).total, &ws))) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = internal_ws(ws_layout(B, H, N, d, dtype).total, s, &ws))) return rc;
     if ((rc = run_prepare(q, k, v, B, H, N, d, SOLATTN_SPARSE, dtype, ws, s, false))) return rc;
     return run_attend(q, k, v, nullptr, B, H, N, d, prefix_len, tau, SOLATTN_SPARSE, dtype, ws, s,
                       mask_out, score_out, thr_out, 1);
@@ -480,6 +548,7 @@ int solattn_probe_mfma_bf16(float* sink, int64_t waves, int64_t iters, void* str
         return fail(SOLATTN_EINVAL, "waves must be in [1, 2^20] (got %lld)", (long long)waves);
     if (iters < 1 || iters > (1LL << 20))
         return fail(SOLATTN_EINVAL, "iters must be in [1, 2^20] (got %lld)", (long long)iters);
+    if (int rc = check_device_ptrs({sink})) return rc;
     const hipError_t e = launch_probe_mfma(sink, waves, iters, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "probe launch");
     return SOLATTN_OK;
@@ -499,6 +568,7 @@ int solattn_pack_qkv_int8(const void* q, const void* k, const void* v, int64_t B
     const size_t tb = (size_t)B * H * Ns * d * 2, sb = (size_t)B * H * Ns * 3 *
                                                          solattn_transport_record_bytes(d);
     if ((rc = check_buffers({q, k, v}, tb, {send}, sb))) return rc;
+    if ((rc = check_device_ptrs({q, k, v, send}))) return rc;
     QkvPackArgs a{q, k, v, static_cast<uint8_t*>(send), B, H, H / P, Ns, P};
     const hipError_t e = launch_pack_qkv_int8(a, (int)d, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SOLATTN_OK : hip_fail(e, "pack kernel launch");
@@ -512,6 +582,7 @@ int solattn_unpack_qkv_int8(const void* recv, int64_t B, int64_t Hp, int64_t Ns,
     const size_t rb = (size_t)P * B * Hp * Ns * 3 * solattn_transport_record_bytes(d),
                  tb = (size_t)B * Hp * P * Ns * d * 2;
     if ((rc = check_buffers({recv}, rb, {q, k, v}, tb))) return rc;
+    if ((rc = check_device_ptrs({recv, q, k, v}))) return rc;
     QkvUnpackArgs a{static_cast<const uint8_t*>(recv), q, k, v, B, Hp, Ns, P};
     const hipError_t e = launch_unpack_qkv_int8(a, (int)d, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SOLATTN_OK : hip_fail(e, "unpack kernel launch");
@@ -525,6 +596,7 @@ int solattn_pack_out_fp8(const void* o, int64_t B, int64_t Hp, int64_t Ns, int64
     const size_t tb = (size_t)B * Hp * P * Ns * d * 2,
                  sb = (size_t)P * B * Hp * Ns * solattn_transport_record_bytes(d);
     if ((rc = check_buffers({o}, tb, {send}, sb))) return rc;
+    if ((rc = check_device_ptrs({o, send}))) return rc;
     OutPackArgs a{o, static_cast<uint8_t*>(send), B, Hp, Ns, P};
     const hipError_t e = launch_pack_out_fp8(a, (int)d, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SOLATTN_OK : hip_fail(e, "pack kernel launch");
@@ -538,6 +610,7 @@ int solattn_unpack_out_fp8(const void* recv, int64_t B, int64_t Hp, int64_t Ns, 
     const size_t rb = (size_t)P * B * Hp * Ns * solattn_transport_record_bytes(d),
                  tb = (size_t)B * P * Hp * Ns * d * 2;
     if ((rc = check_buffers({recv}, rb, {o}, tb))) return rc;
+    if ((rc = check_device_ptrs({recv, o}))) return rc;
     OutUnpackArgs a{static_cast<const uint8_t*>(recv), o, B, Hp, Ns, P};
     const hipError_t e = launch_unpack_out_fp8(a, (int)d, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SOLATTN_OK : hip_fail(e, "unpack kernel launch");

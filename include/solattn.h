@@ -40,9 +40,19 @@
  *   - Every argument is checked on the host before any device call; a
  *     rejected call enqueues nothing and returns a nonzero code whose text
  *     solattn_last_error() gives.
- *   - Calls on different streams may run concurrently, except that the
- *     entry points without a `ws` argument share one internal workspace per
- *     device: concurrent calls of those on different streams race.
+ *   - Calls on different streams may run concurrently.  The entry points
+ *     without a `ws` argument (solattn_forward, solattn_forward_debug,
+ *     solattn_pool, solattn_route) keep one internal workspace per (device,
+ *     stream), grown on demand (a growth allocates once; a buffer once
+ *     handed out is kept, not freed, until the process ends), so their calls
+ *     on different streams never share memory; calls on one stream are
+ *     ordered by the stream.  Because they may allocate, they refuse a
+ *     stream that is being captured into a graph (SOLATTN_EUNSUPPORTED,
+ *     nothing enqueued); under capture use the _ws entry points.
+ *   - Every pointer the kernels will read or write must be device memory
+ *     HIP knows (hipMalloc / torch device tensors; managed memory is
+ *     accepted): host pointers are rejected with SOLATTN_EINVAL before any
+ *     launch.
  */
 #ifndef SOLATTN_H
 #define SOLATTN_H
@@ -116,8 +126,8 @@ extern "C" {
  * Full forward pass: pooling (step 1) then the fused routing + attention
  * kernel (steps 2-5).  In DENSE mode tau and prefix_len are ignored and no
  * pooling is done; in TOPK mode tau is the kept fraction (outside (0, 1]:
- * SOLATTN_EINVAL).  Uses an internal per-device workspace that grows on
- * demand (the growth synchronises the device once).
+ * SOLATTN_EINVAL).  Uses the internal workspace of (current device,
+ * stream), allocated or grown on first need.
  */
 int solattn_forward(const void* q, const void* k, const void* v, void* out, int64_t B,
                     int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau, int mode,

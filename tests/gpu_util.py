@@ -42,13 +42,29 @@ def mask_compare(gmask, ores, b, h):
     return int(diff.sum()), int(near.sum())
 
 
+def max_abs_diff(g, o):
+    """max |g - o| over the elements, +inf as soon as g holds a non-finite
+    value (NaN or inf), so that a caller folding errors with max() -- which
+    drops NaN -- cannot pass on a broken output."""
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    if g.size == 0:
+        return 0.0
+    if not np.isfinite(g).all():
+        return float("inf")
+    return float(np.max(np.abs(g - o)))
+
+
 def out_error(gout, oout, rows=None):
+    """(max abs error, max abs error / max |oracle|) over the rows the
+    oracle produced; both +inf when the GPU rows hold NaN or inf."""
     g, o = gout, oout
     if rows is not None:
         g, o = g[rows], o[rows]
     ok = ~np.isnan(o).any(axis=-1)
     g, o = g[ok], o[ok]
-    return float(np.max(np.abs(g - o))), float(np.max(np.abs(g - o)) / max(np.max(np.abs(o)), 1e-30))
+    ab = max_abs_diff(g, o)
+    return ab, ab / max(float(np.max(np.abs(o))) if o.size else 0.0, 1e-30)
 
 
 def block_rows(blocks, N):

@@ -2,7 +2,9 @@
 streams, and captured into a HIP graph: the workspace entry points allocate
 nothing and enqueue only kernels on the caller's stream, so each of these
 must reproduce the default-stream result bit for bit (the kernels are
-deterministic)."""
+deterministic).  The plain entry points keep one internal workspace per
+(device, stream): concurrent plain calls on two streams must also reproduce
+their single-stream results, and under graph capture they refuse to run."""
 import numpy as np
 import pytest
 
@@ -20,8 +22,9 @@ def _gpu():
 
 
 def _case(seed, N=3000, H=4):
+    grid = (-(-(N - 128) // (24 * 60)), 24, 60)
     q, k, v = inputs.custom(1, H, N, 128, "bf16", prefix_len=128, seed=seed, kind="field",
-                            grid=(2, 24, 60))
+                            grid=grid)
     return device_tensors(q, k, v, "bf16")
 
 
@@ -133,3 +136,60 @@ def test_fused_producer_on_a_side_stream():
     side.synchronize()
     assert torch.equal(q1, q0) and torch.equal(o1, o0)
     assert torch.equal(ws1, ws0)
+
+
+def test_plain_forward_on_two_streams_concurrently():
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    cases = [_case(87, N=6000, H=8), _case(88, N=2500, H=8)]
+    refs = [sa.solattn_forward(*c, None, 128, 1.25, "sparse").clone() for c in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.full_like(c[0], float("nan")) for c in cases]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(4):
+        for c, s, o in zip(cases, streams, outs):
+            with torch.cuda.stream(s):
+                sa.solattn_forward(*c, o, 128, 1.25, "sparse")
+    for s in streams:
+        s.synchronize()
+    for o, r in zip(outs, refs):
+        assert torch.equal(o, r)
+    # the routing exports of the plain debug entry point, also on two streams
+    dbg = [None, None]
+    for n, (c, s) in enumerate(zip(cases, streams)):
+        with torch.cuda.stream(s):
+            dbg[n] = sa.solattn_forward_debug(*c, None, 128, 1.25, "sparse")
+    for s in streams:
+        s.synchronize()
+    for (o, words, sc, th), r in zip(dbg, refs):
+        assert torch.equal(o, r)
+
+
+def test_plain_entry_points_refuse_capture():
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    qd, kd, vd = _case(89)
+    out = torch.empty_like(qd)
+    x = torch.zeros(16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    codes = []
+    calls = (lambda: sa.solattn_forward(qd, kd, vd, out, 128, 1.25, "sparse"),
+             lambda: sa.solattn_pool(qd, kd, vd),
+             lambda: sa.solattn_route(qd, kd, vd, 128, 1.25, want_scores=False))
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for call in calls:
+                try:
+                    call()
+                except sa.SolAttnError as e:
+                    codes.append(e.code)
+            x.add_(1)
+    torch.cuda.synchronize()
+    assert codes == [sa.EUNSUPPORTED] * len(calls)
+    g.replay()
+    torch.cuda.synchronize()
+    assert bool(x.eq(1).all())

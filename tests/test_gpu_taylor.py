@@ -11,7 +11,7 @@ import pytest
 import oracle
 from oracle import taylor as OT
 from block_sparse_video_solattn_amd import inputs
-from gpu_util import TOL_BF16_ABS, device_tensors, mask_compare
+from gpu_util import TOL_BF16_ABS, device_tensors, mask_compare, max_abs_diff
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +53,7 @@ def test_taylor_matches_oracle(B, H, N, d, prefix, tau, kind):
             mask_compare(gmask, ro, b, h)
             r = OT.head(q[b, h], k[b, h], v[b, h], prefix, tau, order=1,
                         mask_override=gmask[b, h])
-            worst = max(worst, float(np.abs(g[b, h] - r["out"]).max()))
+            worst = max(worst, max_abs_diff(g[b, h], r["out"]))
     assert worst <= TOL_BF16_ABS, worst
 
 
