@@ -45,6 +45,7 @@ _SZ = ctypes.c_size_t
 _SIGS = {
     "solattn_forward": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P], _I),
     "solattn_workspace_bytes": ([_I64, _I64, _I64, _I64, _I], _SZ),
+    "solattn_forward_noalloc": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P], _I),
     "solattn_forward_ws": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P, _SZ, _P], _I),
     "solattn_prepare_ws": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I, _I, _P, _SZ, _P], _I),
     "solattn_attend_ws": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P, _SZ, _P], _I),
@@ -192,6 +193,22 @@ def solattn_forward(q, k, v, out=None, prefix_len: int = 0, tau: float = 1.0, mo
     _check(_lib.solattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, prefix_len,
                                 float(tau), _mode_code(mode), _dtype_code(q), _stream(stream)))
     return out
+
+
+def solattn_forward_noalloc(q, k, v, out, prefix_len: int, tau: float, mode="sparse",
+                            stream=None):
+    """solattn_forward with the library's fixed device workspace (no
+    allocation in the call; shapes beyond SOLATTN_NOALLOC_SCRATCH_BYTES of
+    workspace are rejected).  Calls that overlap on one GPU race."""
+    B, H, N, d = _shape(q)
+    _check_like(q, k, v, out)
+    _check(_lib.solattn_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d,
+                                        prefix_len, float(tau), _mode_code(mode),
+                                        _dtype_code(q), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def solattn_forward_ws(q, k, v, out, prefix_len, tau, mode, ws, stream=None):

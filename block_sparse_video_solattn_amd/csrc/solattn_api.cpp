@@ -222,6 +222,35 @@ int internal_ws(size_t need, hipStream_t stream, void** out) {
     return SOLATTN_OK;
 }
 
+// Workspace of solattn_forward_noalloc: a fixed device array, so that the
+// call allocates nothing.  Each device holds its own copy (from the load of
+// the library's device code until the process ends); host code must not use
+// the array's name as an address -- it is a host-side stand-in -- but the
+// per-device address from hipGetSymbolAddress, resolved on the first call
+// on each device.  Nothing in it needs to start at zero: every byte the
+// attention kernel reads is written earlier in the same call by the
+// pooling pass (padding included).
+__device__ __align__(256) unsigned char scratch[SOLATTN_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mutex;
+std::vector<void*> g_scratch_ptr;  // per device; NULL until resolved
+
+int scratch_ptr(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(SOLATTN_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SOLATTN_OK;
+}
+
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 PoolArgs pool_args(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t N,
@@ -449,6 +478,26 @@ int solattn_forward(const void* q, const void* k, const void* v, void* out, int6
     if ((rc = internal_ws(need, static_cast<hipStream_t>(stream), &ws))) return rc;
     return solattn_forward_ws(q, k, v, out, B, H, N, d, prefix_len, tau, mode, dtype, ws, need,
                               stream);
+}
+
+int solattn_forward_noalloc(const void* q, const void* k, const void* v, void* out, int64_t B,
+                            int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau,
+                            int mode, int dtype, void* stream) {
+    int rc = validate(q, k, v, out, true, B, H, N, d, prefix_len, tau, mode, dtype);
+    if (rc) return rc;
+    const size_t need = ws_layout(B, H, N, d, dtype).total;
+    if (need > (size_t)SOLATTN_NOALLOC_SCRATCH_BYTES)
+        return fail(SOLATTN_EUNSUPPORTED,
+                    "this shape needs %zu bytes of workspace; solattn_forward_noalloc holds %zu "
+                    "(use solattn_forward_ws)",
+                    need, (size_t)SOLATTN_NOALLOC_SCRATCH_BYTES);
+    if ((rc = check_device_ptrs({q, k, v, out}))) return rc;
+    void* ws = nullptr;
+    if ((rc = scratch_ptr(&ws))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = run_prepare(q, k, v, B, H, N, d, mode, dtype, ws, s, true))) return rc;
+    return run_attend(q, k, v, out, B, H, N, d, prefix_len, tau, mode, dtype, ws, s, nullptr,
+                      nullptr, nullptr, 0);
 }
 
 int solattn_prepare_ws(const void* q, const void* k, const void* v, int64_t B, int64_t H,

@@ -48,7 +48,8 @@
  *     on different streams never share memory; calls on one stream are
  *     ordered by the stream.  Because they may allocate, they refuse a
  *     stream that is being captured into a graph (SOLATTN_EUNSUPPORTED,
- *     nothing enqueued); under capture use the _ws entry points.
+ *     nothing enqueued); under capture use the _ws entry points or
+ *     solattn_forward_noalloc.
  *   - Every pointer the kernels will read or write must be device memory
  *     HIP knows (hipMalloc / torch device tensors; managed memory is
  *     accepted): host pointers are rejected with SOLATTN_EINVAL before any
@@ -145,6 +146,28 @@ size_t solattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int d
 int solattn_forward_ws(const void* q, const void* k, const void* v, void* out, int64_t B,
                        int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau, int mode,
                        int dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * solattn_forward for callers that cannot allocate device memory at call
+ * time: code being captured into a HIP graph, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments, modes, results and
+ * errors as solattn_forward (the same kernels run), but the workspace is a
+ * fixed array of SOLATTN_NOALLOC_SCRATCH_BYTES bytes in the library's device
+ * code, one copy per GPU held until the process ends, so the call
+ * allocates nothing and enqueues only kernels on `stream`.  Shapes whose
+ * workspace (solattn_workspace_bytes) exceeds it -- e.g. B=1, H=32,
+ * N=16384, d=128 in bf16 -- are rejected with SOLATTN_EUNSUPPORTED before
+ * any device call; 64 MiB covers, for instance, one GPU's four heads of
+ * that shape (H=4).  Every call on one GPU uses the same array: calls that
+ * overlap in time on one GPU (two streams, two host threads) race and must
+ * be serialised by the caller.  The first call on each GPU resolves the
+ * array's device address (a runtime query that may load the library's
+ * device code): make it once before capturing.
+ */
+#define SOLATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int solattn_forward_noalloc(const void* q, const void* k, const void* v, void* out,
+                            int64_t B, int64_t H, int64_t N, int64_t d, int64_t prefix_len,
+                            float tau, int mode, int dtype, void* stream);
 
 /*
  * The two stages of solattn_forward_ws as separate launches, so that each

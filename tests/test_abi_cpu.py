@@ -92,6 +92,18 @@ def test_other_entry_points_validate(lib):
                         None) == 1
 
 
+def test_noalloc_rejects_oversize_shapes_on_host(lib):
+    # the fixed workspace of solattn_forward_noalloc: a shape that needs more
+    # is refused before any device call (fake addresses, never dereferenced)
+    f = ctypes.c_float
+    call = lambda H, N: lib.raw_call("solattn_forward_noalloc", A, A + 0x10000000, A + 0x20000000,
+                                     A + 0x30000000, 1, H, N, 128, 0, f(1.0), 1, 1, None)
+    assert lib.solattn_workspace_bytes(1, 32, 16384, 128, 1) > lib.NOALLOC_SCRATCH_BYTES
+    assert call(32, 16384) == lib.EUNSUPPORTED
+    assert "workspace" in lib.solattn_last_error()
+    assert call(0, 16384) == lib.EINVAL
+
+
 def test_import_without_library_fails_loudly(tmp_path):
     # a copy of the Python package without the shared library refuses to import
     import shutil
