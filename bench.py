@@ -19,10 +19,11 @@ sys.path.insert(0, ROOT)
 METRIC = "ms/call + dense-equiv TFLOP/s and % bf16 MFMA peak on kept tiles, N=16128 refine"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 SEED = 3000
 # extra legs after the headline measurement, in run order
 LEGS = ("mfma_probe", "dense_sweep", "torch_sdpa", "taylor1", "setup", "sp_rank_p8",
-        "qk_producer", "sparsity_90_check", "long_clip")
+        "qk_producer", "sparsity_90_check", "long_clip", "small_configs")
 SEED_LONG = 5000
 
 # HBM traffic of one attention dispatch from rocprofv3 counters on this
@@ -33,8 +34,9 @@ SEED_LONG = 5000
 # reported as null until the counters are taken again.
 ATTN_COUNTERS = {
     "sources_sha256": "5cb729acb4f2fd90756e48decfb551c2fdc5b818ffc7853c76142ac1c41cf568",
-    "fetch_kib": 738077.3, "fetch_scale": 2.0,
-    "write_kib": 131079.6, "write_scale": 1.0,
+    "fetch_kib": 735355.9, "fetch_scale": 2.0,
+    "write_kib": 131080.4, "write_scale": 1.0,
+    "profile": "profiles/attn_bf16_refine_tau1.25_counters.txt",
 }
 ATTN_SOURCES = ("attn_bf16.hip", "route.h", "common.h", "launch.h", "taylor.h")
 
@@ -85,15 +87,26 @@ def time_calls(fn, n, stream):
     return [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
 
 
-def cpu_baseline(q, k, v, w, tau, budget_s=15.0):
-    """The fp64 oracle (as it stands) on whole heads until ~budget_s of work,
-    scaled to one call over all heads."""
+def _oracle_heads(q, k, v, prefix_len, tau, heads, threads):
     import oracle
+    t0 = time.time()
+    for h in heads:
+        oracle.head(q[0, h], k[0, h], v[0, h], prefix_len, tau, threads=threads)
+    return time.time() - t0
+
+
+def cpu_baseline(q, k, v, w, tau, budget_s=15.0):
+    """The fp64 oracle (as it stands) on whole heads of the headline call
+    until ~budget_s of work, scaled to one call over all heads; then the
+    other workloads: tiny and small in full, draft and long on heads
+    {0, 15, 31} scaled by H/3 (labelled extrapolated)."""
+    import oracle  # noqa: F401
+    from block_sparse_video_solattn_amd import inputs
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
     t0 = time.time()
     heads = 0
     for h in range(w.H):
-        oracle.head(q[0, h], k[0, h], v[0, h], w.prefix_len, tau, threads=threads)
+        _oracle_heads(q, k, v, w.prefix_len, tau, [h], threads)
         heads += 1
         if time.time() - t0 > budget_s:
             break
@@ -104,16 +117,40 @@ def cpu_baseline(q, k, v, w, tau, budget_s=15.0):
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
+    per = {}
+    draft_tau = None
+    try:
+        with open(os.path.join(ROOT, "tests", "golden", "draft_tau.json")) as f:
+            cal = json.load(f)
+        draft_tau, draft_seed = float(cal["tau"]), int(cal["seed"])
+    except OSError:
+        pass
+    for name, seed, tau_w, sample in (("tiny", 1000, 1.0, None), ("small", 2000, 1.25, None),
+                                      ("draft", None, draft_tau, (0, 15, 31)),
+                                      ("long", SEED_LONG, 1.5, (0, 15, 31))):
+        if tau_w is None:
+            continue
+        wl = inputs.WORKLOADS[name]
+        hs = list(range(wl.H)) if sample is None else list(sample)
+        qq, kk, vv = inputs.make_inputs(wl, draft_seed if name == "draft" else seed, heads=hs)
+        sec = _oracle_heads(qq, kk, vv, wl.prefix_len, tau_w, range(len(hs)), threads)
+        per[name] = {"ms_per_call": round(sec / len(hs) * wl.H * 1000.0, 1), "tau": tau_w,
+                     "heads_timed": len(hs), "heads": wl.H,
+                     "kind": "full call" if sample is None else
+                             "extrapolated: heads %s timed, scaled by %d/%d" % (
+                                 ",".join(map(str, hs)), wl.H, len(hs))}
     return {"value": round(dt / heads * w.H * 1000.0, 1), "unit": "ms/call", "cores": threads,
             "kind": "oracle", "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": "%d of %d heads of the same refine call (sparse, tau=%g, all query blocks), "
-                      "scaled by %d/%d" % (heads, w.H, tau, w.H, heads)}
+                      "scaled by %d/%d" % (heads, w.H, tau, w.H, heads),
+            "other_workloads": per}
 
 
 def draft_check(sa, stream):
     """The draft-stage shape at the tau whose video block sparsity is ~90 %
     (tests/golden/draft_tau.json, calibrated with the oracle's routing):
-    sparse and dense calls timed in the same run."""
+    sparse and dense calls timed in the same run, with the attention
+    kernel's kept-tile rate."""
     import numpy as np
     import torch
     from block_sparse_video_solattn_amd import inputs
@@ -131,10 +168,17 @@ def draft_check(sa, stream):
     words, _, _ = sa.solattn_route(qd, kd, vd, w.prefix_len, tau, want_scores=False)
     torch.cuda.synchronize()
     m = sa.unpack_mask(words, w.nb)
+    fk, fp = kept_flops(m, w.N, w.D)
     pb = (w.prefix_len + 63) // 64
 
     def sparse():
         sa.solattn_forward_ws(qd, kd, vd, out, w.prefix_len, tau, "sparse", ws)
+
+    def prep():
+        sa.solattn_prepare_ws(qd, kd, vd, "sparse", ws)
+
+    def attend():
+        sa.solattn_attend_ws(qd, kd, vd, out, w.prefix_len, tau, "sparse", ws)
 
     def dense():
         sa.solattn_forward_ws(qd, kd, vd, out, w.prefix_len, 0.0, "dense", ws)
@@ -145,17 +189,107 @@ def draft_check(sa, stream):
     for _ in range(3):
         sparse()
     sms = float(np.median(time_calls(sparse, 20, stream)))
+    prep()
+    ams = float(np.median(time_calls(attend, 20, stream)))
     for _ in range(3):
         topk()
     tms = float(np.median(time_calls(topk, 20, stream)))
     dense()
     dms = float(np.median(time_calls(dense, 5, stream)))
+    kept_tflops = fk / (ams * 1e-3) / 1e12
     return {"workload": "draft: 672x384 -> 32x24x42 latent, 512 prefix + 32256 video tokens",
             "N": w.N, "tau": tau, "video_sparsity": round(float(1 - m[..., pb:].mean()), 4),
-            "sparse_ms": round(sms, 4), "dense_ms": round(dms, 3),
+            "sparse_ms": round(sms, 4), "attn_ms": round(ams, 4), "dense_ms": round(dms, 3),
             "speedup_vs_dense": round(dms / sms, 2),
+            "dense_equiv_tflops": round(4.0 * w.B * w.H * w.N * w.N * w.D / (sms * 1e-3) / 1e12, 1),
+            "kept_tile_tflop": round(fk / 1e12, 4), "pooled_tflop": round(fp / 1e12, 5),
+            "attn_kept_tflops": round(kept_tflops, 1),
+            "kept_tile_mfma_frac": round(kept_tflops / PEAK_BF16_TFLOPS, 4),
             "fixed_ratio_10pct": {"mode": "topk", "keep_fraction": 0.1, "ms": round(tms, 4),
                                   "speedup_vs_dense": round(dms / tms, 2)}}
+
+
+def route_bytes(B, H, N, d):
+    """Algorithmic bytes of the scoring pass (solattn_route_ws without
+    exports): the fp32 pooled queries and the transposed pooled keys, read
+    once (B*H*Nb*d*4 + B*H*d*Nbp*4); nothing is written."""
+    nb = (N + 63) // 64
+    nbp = (nb + 63) // 64 * 64
+    return B * H * nb * d * 4 + B * H * d * nbp * 4
+
+
+def route_l2_bytes(B, H, N, d):
+    """Bytes the scoring pass reads from L2: the transposed pooled keys once
+    per group of four query blocks, plus the pooled queries."""
+    nb = (N + 63) // 64
+    nbp = (nb + 63) // 64 * 64
+    return B * H * ((nb + 3) // 4) * d * nbp * 4 + B * H * nb * d * 4
+
+
+def scoring_pass(sa, stream, qd, w, tau, ws):
+    """Time solattn_route_ws (the scoring and threshold pass alone, no
+    exports) on a workspace prepared for the same inputs."""
+    import numpy as np
+
+    def route():
+        sa.solattn_route_ws(qd, w.prefix_len, tau, ws)
+    route()
+    ms = float(np.median(time_calls(route, 20, stream)))
+    return {"ms": round(ms, 4),
+            "GBps": round(route_bytes(w.B, w.H, w.N, w.D) / (ms * 1e-3) / 1e9, 1),
+            "l2_read_GBps": round(route_l2_bytes(w.B, w.H, w.N, w.D) / (ms * 1e-3) / 1e9, 1)}
+
+
+def small_configs_check(sa, stream):
+    """The tiny (fp32) and small (bf16) workloads: per-call time, dense
+    equivalent rate and the attention kernel's kept-tile rate, with the
+    dense mode beside them.  (Few workgroups: launch-bound shapes.)"""
+    import numpy as np
+    import torch
+    from block_sparse_video_solattn_amd import inputs
+    res = {}
+    for name, seed, tau in (("tiny", 1000, 1.0), ("small", 2000, 1.25)):
+        w = inputs.WORKLOADS[name]
+        td = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        q, k, v = inputs.make_inputs(w, seed)
+        qd, kd, vd = [torch.from_numpy(x).to("cuda").to(td).contiguous() for x in (q, k, v)]
+        out = torch.empty_like(qd)
+        ws = torch.empty(sa.solattn_workspace_bytes(w.B, w.H, w.N, w.D, td), dtype=torch.uint8,
+                         device="cuda")
+        words, _, _ = sa.solattn_route(qd, kd, vd, w.prefix_len, tau, want_scores=False)
+        torch.cuda.synchronize()
+        m = sa.unpack_mask(words, w.nb)
+        fk, fp = kept_flops(m, w.N, w.D)
+
+        def call():
+            sa.solattn_forward_ws(qd, kd, vd, out, w.prefix_len, tau, "sparse", ws)
+
+        def attend():
+            sa.solattn_attend_ws(qd, kd, vd, out, w.prefix_len, tau, "sparse", ws)
+
+        def dense():
+            sa.solattn_forward_ws(qd, kd, vd, out, w.prefix_len, 0.0, "dense", ws)
+        for _ in range(5):
+            call()
+        cms = float(np.median(time_calls(call, 50, stream)))
+        ams = float(np.median(time_calls(attend, 50, stream)))
+        dense()
+        dms = float(np.median(time_calls(dense, 20, stream)))
+        kt = fk / (ams * 1e-3) / 1e12
+        pb = (w.prefix_len + 63) // 64
+        e = {"B": w.B, "H": w.H, "N": w.N, "d": w.D, "dtype": w.dtype, "tau": tau,
+             "video_sparsity": round(float(1 - m[..., pb:].mean()), 4),
+             "ms_per_call": round(cms, 4), "attn_ms": round(ams, 4), "dense_ms": round(dms, 4),
+             "speedup_vs_dense": round(dms / cms, 2),
+             "dense_equiv_tflops": round(4.0 * w.B * w.H * w.N * w.N * w.D / (cms * 1e-3) / 1e12, 2),
+             "attn_kept_tflops": round(kt, 2), "workgroups": int(w.B * w.H * w.nb)}
+        if w.dtype == "bf16":
+            e["kept_tile_mfma_frac"] = round(kt / PEAK_BF16_TFLOPS, 4)
+        else:
+            e["kept_tile_frac_of_fp32_vector_peak"] = round(kt / PEAK_F32_TFLOPS, 4)
+        res[name] = e
+        del qd, kd, vd, out, ws
+    return res
 
 
 def pool_bytes(B, H, N, d):
@@ -212,6 +346,8 @@ def long_clip_check(sa, stream):
         sa.solattn_route(qd, kd, vd, w.prefix_len, tau, want_scores=False, mask=mw, thr=th)
     setup()
     sms = float(np.median(time_calls(setup, 10, stream)))
+    prep()
+    score = scoring_pass(sa, stream, qd, w, tau, ws)
     tflops = fk / (ams * 1e-3) / 1e12
     return {"workload": "long clip: 15 s at 1344x768 -> 46x24x42 latent, 2048 prefix + 46368 "
                         "video tokens", "N": w.N, "tau": tau,
@@ -221,6 +357,7 @@ def long_clip_check(sa, stream):
             "pool_ms": round(pms, 4),
             "pool_GBps": round(pool_bytes(w.B, w.H, w.N, w.D) / (pms * 1e-3) / 1e9, 1),
             "setup_ms": round(sms, 4),
+            "scoring_pass": score,
             "attn_ms": round(ams, 4),
             "kept_tile_tflop": round(fk / 1e12, 4), "pooled_tflop": round(fp / 1e12, 5),
             "attn_kept_tflops": round(tflops, 1),
@@ -549,7 +686,8 @@ def main():
         "pooled_tflop": round(fp / 1e12, 5),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": attn_traffic_bytes(), "kernel": "attn_bf16_kernel<128>"},
+                     "traffic": attn_traffic_bytes(), "kernel": "attn_bf16_kernel<128>",
+                     "traffic_source": ATTN_COUNTERS["profile"] if attn_traffic_bytes() else None},
     }
 
     if "mfma_probe" in legs:
@@ -624,6 +762,9 @@ def main():
             sa.solattn_route(qd, kd, vd, w.prefix_len, tau, want_scores=False, mask=mw, thr=th)
         setup()
         res["setup_ms"] = round(float(np.median(time_calls(setup, 20, stream))), 4)
+        # the scoring / threshold pass alone, on the headline call's workspace
+        sa.solattn_prepare_ws(qd, kd, vd, "sparse", ws)
+        res["scoring_pass"] = scoring_pass(sa, stream, qd, w, tau, ws)
     if "sp_rank_p8" in legs:
         res["sp_rank_p8"] = sp_rank_check(sa, stream, qd, kd, vd, w.prefix_len, tau)
     del qd, kd, vd, out, ws, dev
@@ -636,6 +777,9 @@ def main():
         torch.cuda.empty_cache()
     if "long_clip" in legs:
         res["long_clip"] = long_clip_check(sa, stream)
+        torch.cuda.empty_cache()
+    if "small_configs" in legs:
+        res["small_configs"] = small_configs_check(sa, stream)
 
     if not args.no_cpu:
         log("timing the CPU oracle baseline")

@@ -10,7 +10,7 @@ _BINDING_NAMES = (
     "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "ENOMEM", "NOALLOC_SCRATCH_BYTES",
     "SolAttnError", "solattn_attend_ws", "solattn_forward_noalloc",
     "solattn_forward", "solattn_forward_debug", "solattn_forward_ws", "solattn_last_error",
-    "solattn_pool", "solattn_prepare_ws", "solattn_probe_mfma_bf16", "solattn_route",
+    "solattn_pool", "solattn_prepare_ws", "solattn_probe_mfma_bf16", "solattn_route", "solattn_route_ws",
     "solattn_strerror",
     "solattn_version", "solattn_workspace_bytes", "unpack_mask", "raw_call",
     "solattn_transport_record_bytes", "solattn_pack_qkv_int8", "solattn_unpack_qkv_int8",

@@ -52,6 +52,7 @@ _SIGS = {
     "solattn_forward_debug": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P, _P, _P, _P], _I),
     "solattn_pool": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P], _I),
     "solattn_route": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _P, _P, _P, _P], _I),
+    "solattn_route_ws": ([_P, _I64, _I64, _I64, _I64, _I64, _F, _I, _P, _SZ, _P, _P, _P, _P], _I),
     "solattn_probe_mfma_bf16": ([_P, _I64, _I64, _P], _I),
     "solattn_transport_record_bytes": ([_I64], _SZ),
     "solattn_pack_qkv_int8": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P], _I),
@@ -285,6 +286,19 @@ def solattn_route(q, k, v, prefix_len: int, tau: float, stream=None, want_scores
         _same_device(q, t, name)
     _check(_lib.solattn_route(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, prefix_len, float(tau),
                               _dtype_code(q), _ptr(mask), _ptr(scores), _ptr(thr), _stream(stream)))
+    return mask, scores, thr
+
+
+def solattn_route_ws(q, prefix_len: int, tau: float, ws, mask=None, scores=None, thr=None,
+                     stream=None):
+    """The scoring / threshold pass alone on a workspace solattn_prepare_ws
+    filled (sparse mode) for q's shape; writes the given exports (any None)."""
+    B, H, N, d = _shape(q)
+    for t, name in ((mask, "mask"), (scores, "scores"), (thr, "thr")):
+        _same_device(q, t, name)
+    _check(_lib.solattn_route_ws(_ptr(q), B, H, N, d, prefix_len, float(tau), _dtype_code(q),
+                                 _ptr(ws), _ws_bytes(q, ws), _ptr(mask), _ptr(scores), _ptr(thr),
+                                 _stream(stream)))
     return mask, scores, thr
 
 

@@ -576,6 +576,19 @@ int solattn_route(const void* q, const void* k, const void* v, int64_t B, int64_
                       mask_out, score_out, thr_out, 1);
 }
 
+int solattn_route_ws(const void* q, int64_t B, int64_t H, int64_t N, int64_t d,
+                     int64_t prefix_len, float tau, int dtype, const void* ws, size_t ws_bytes,
+                     uint32_t* mask_out, float* score_out, float* thr_out, void* stream) {
+    // reads only the pooled means in ws; q stands in for k and v in the checks
+    int rc = validate(q, q, q, nullptr, false, B, H, N, d, prefix_len, tau, SOLATTN_SPARSE, dtype);
+    if (rc) return rc;
+    if ((rc = check_ws(const_cast<void*>(ws), ws_bytes, B, H, N, d, dtype))) return rc;
+    if ((rc = check_device_ptrs({ws, mask_out, score_out, thr_out}))) return rc;
+    return run_attend(q, q, q, nullptr, B, H, N, d, prefix_len, tau, SOLATTN_SPARSE, dtype,
+                      const_cast<void*>(ws), static_cast<hipStream_t>(stream), mask_out, score_out,
+                      thr_out, 1);
+}
+
 const char* solattn_strerror(int code) {
     switch (code) {
         case SOLATTN_OK: return "ok";

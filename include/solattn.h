@@ -215,6 +215,19 @@ int solattn_route(const void* q, const void* k, const void* v, int64_t B, int64_
                   int64_t N, int64_t d, int64_t prefix_len, float tau, int dtype,
                   uint32_t* mask_out, float* score_out, float* thr_out, void* stream);
 
+/*
+ * Step 2 alone on a workspace that solattn_prepare_ws (SPARSE or TOPK mode,
+ * same shape and dtype) has filled: the block scores, thresholds and keep
+ * bits of every query block, with the exports of solattn_forward_debug (any
+ * may be NULL).  The scoring pass on its own (page "Sol-H3" news, kocpc,
+ * section "技術組成", reports the routing setup time on its own); reads only
+ * the pooled means in ws, so q serves for the shape and alignment checks
+ * only.  Allocates nothing.
+ */
+int solattn_route_ws(const void* q, int64_t B, int64_t H, int64_t N, int64_t d,
+                     int64_t prefix_len, float tau, int dtype, const void* ws, size_t ws_bytes,
+                     uint32_t* mask_out, float* score_out, float* thr_out, void* stream);
+
 /* Static text of a return code. */
 const char* solattn_strerror(int code);
 

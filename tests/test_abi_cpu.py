@@ -90,6 +90,10 @@ def test_other_entry_points_validate(lib):
     assert lib.raw_call("solattn_pool", A, A, A, None, None, None, 1, 1, 64, 32, 1, None) == 1
     assert lib.raw_call("solattn_route", A, A, A, 1, 1, 64, 64, 65, f(1.0), 1, None, None, None,
                         None) == 1
+    assert lib.raw_call("solattn_route_ws", A, 1, 1, 64, 64, 0, f(1.0), 1, None, 1 << 30, None,
+                        None, None, None) == 1                       # NULL ws
+    assert lib.raw_call("solattn_route_ws", A, 1, 1, 64, 64, 0, f(1.0), 1, A, 16, None, None,
+                        None, None) == 1                             # too small
 
 
 def test_noalloc_rejects_oversize_shapes_on_host(lib):

@@ -8,8 +8,8 @@ import pytest
 
 import oracle
 from block_sparse_video_solattn_amd import inputs
-from gpu_util import (TOL_BF16_ABS, TOL_F32_REL, block_rows, device_tensors, gpu_debug,
-                      mask_compare, out_error)
+from gpu_util import (POOLED_GATE, TOL_BF16_ABS, TOL_F32_REL, block_rows, device_tensors,
+                      gpu_debug, mask_compare, out_error, pooled_gate)
 
 pytestmark = pytest.mark.gpu
 
@@ -273,6 +273,35 @@ def test_video_stats_without_video_blocks():
     assert st["mask"].all()
 
 
+@pytest.mark.parametrize("N,tau", [(64 * 30 + 8, math.inf), (64 * 30 + 8, 1.0),
+                                   (64 * 130 + 8, 1.0), (64 * 130 + 8, math.inf)])
+def test_pooled_terms_gate_ragged_tail(N, tau):
+    # bf16 outputs, every row: the GPU must sit far closer to the full oracle
+    # than the pooled terms move the rows (POOLED_GATE), with an 8-key tail
+    # block skipped by some or all rows and one to three pooled tiles -- a
+    # dropped pooled tile or the tail block weighted as a full one fails
+    # here (measured with the oracle on the CPU), not only the absolute bound
+    grid = (1, -(-(N - 64) // 64), 64)
+    q, k, v = inputs.custom(1, 2, N, 128, "bf16", prefix_len=64, seed=N % 97 + 3, kind="field",
+                            grid=grid)
+    gout, gmask, _, _ = gpu_debug(q, k, v, "bf16", 64, tau)
+    assert (~gmask[..., -1]).any()
+    if math.isinf(tau):
+        assert not gmask[..., 1:].any()
+    for h in range(2):
+        mo = gmask[0, h].astype(np.uint8)
+        full = oracle.head(q[0, h], k[0, h], v[0, h], 64, float(np.float32(tau)),
+                           mask_override=mo)["out"]
+        nopool = oracle.head(q[0, h], k[0, h], v[0, h], 64, 0.5, mode=oracle.TOPK,
+                             mask_override=mo)["out"]
+        ab, _ = out_error(gout[0, h], full)
+        sg, med = pooled_gate(gout[0, h], full, nopool)
+        print("N=%d tau=%g head %d: max abs err %.3g, median pooled distance %.3g, gate %.4f"
+              % (N, tau, h, ab, med, sg))
+        assert ab <= TOL_BF16_ABS
+        assert sg <= POOLED_GATE, sg
+
+
 def test_pooled_only_path_f32():
     q, k, v = inputs.custom(1, 1, 1024, 64, "f32", seed=34)
     check_forward(q, k, v, "f32", 0, math.inf)
@@ -318,8 +347,16 @@ def test_route_only_matches_debug_forward(H, N, d, dtype):
     qd, kd, vd = device_tensors(q, k, v, dtype)
     _, w1, s1, t1 = sa.solattn_forward_debug(qd, kd, vd, None, 128, 1.25)
     w2, s2, t2 = sa.solattn_route(qd, kd, vd, 128, 1.25)
+    # the scoring pass alone on a prepared workspace: the same exports
+    ws = torch.empty(sa.solattn_workspace_bytes(1, H, N, d, qd.dtype), dtype=torch.uint8,
+                     device="cuda")
+    sa.solattn_prepare_ws(qd, kd, vd, "sparse", ws)
+    w3, s3, t3 = (torch.zeros_like(w2), torch.full_like(s2, float("nan")),
+                  torch.full_like(t2, float("nan")))
+    sa.solattn_route_ws(qd, 128, 1.25, ws, w3, s3, t3)
     torch.cuda.synchronize()
     assert torch.equal(w1, w2) and torch.equal(s1, s2) and torch.equal(t1, t2)
+    assert torch.equal(w3, w2) and torch.equal(s3, s2) and torch.equal(t3, t2)
 
 
 def test_invalid_arguments_on_gpu_enqueue_nothing():

@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 from block_sparse_video_solattn_amd import inputs
-from gpu_util import TOL_BF16_ABS, block_rows, device_tensors, mask_compare, out_error
+from gpu_util import (POOLED_GATE, TOL_BF16_ABS, block_rows, device_tensors, mask_compare,
+                      out_error, pooled_gate)
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -73,15 +74,27 @@ def run_workload(name, seed, tau, heads, block_step, mode="sparse"):
     assert gmask[..., :pb].all()
     blocks = sorted(set(list(range(0, nb, block_step)) + [nb - 1]))
     g = out.float().cpu().numpy()
-    worst = 0.0
+    rows = block_rows(blocks, w.N)
+    pooled = mode.startswith("sparse")
+    worst = gate = 0.0
     for h in heads:
+        mo = gmask[0, h].astype(np.uint8)
         r = oracle.head(q[0, h], k[0, h], v[0, h], w.prefix_len, otau, mode=omode,
-                        mask_override=gmask[0, h].astype(np.uint8), qblocks=blocks)
-        ab, _ = out_error(g[0, h].astype(np.float64), r["out"], block_rows(blocks, w.N))
+                        mask_override=mo, qblocks=blocks)
+        ab, _ = out_error(g[0, h].astype(np.float64), r["out"], rows)
         worst = max(worst, ab)
-    print("%s %s tau=%g: video skip %.4f, mask diffs %d (near-threshold %d), max abs err %.4g"
-          % (name, mode, tau, 1 - gmask[..., pb:].mean(), n_diff, n_near, worst))
+        if pooled:
+            # the same rows with every pooled term dropped (the fixed-ratio
+            # mode's arithmetic on the same mask)
+            r0 = oracle.head(q[0, h], k[0, h], v[0, h], w.prefix_len, 0.5, mode=oracle.TOPK,
+                             mask_override=mo, qblocks=blocks)
+            sg, _ = pooled_gate(g[0, h][rows], r["out"][rows], r0["out"][rows])
+            gate = max(gate, sg)
+    print("%s %s tau=%g: video skip %.4f, mask diffs %d (near-threshold %d), max abs err %.4g, "
+          "pooled gate %.4f" % (name, mode, tau, 1 - gmask[..., pb:].mean(), n_diff, n_near, worst,
+                                gate))
     assert worst <= TOL_BF16_ABS
+    assert gate <= POOLED_GATE, gate
     return gmask
 
 
