@@ -399,14 +399,26 @@ def sp_rank_check(sa, stream, q_all, k_all, v_all, prefix_len, tau, P=8):
     orecv = osend.clone()   # stands in for the chunks arriving from the P head groups
     ob = torch.empty((B, P * Hp, Ns, d), dtype=torch.bfloat16, device="cuda")
     t["unpack_out_fp8"] = lambda: sa.solattn_unpack_out_fp8(orecv, d, o=ob)
+    # the receive side fused with pooling: dequantize the records in the
+    # pooling pass (q' and the workspace), then the attention alone
+    qf = torch.empty_like(q8)
+    outf = torch.empty_like(q8)
+    fused = {
+        "fused_unpack_prepare": lambda: sa.solattn_prepare_int8_ws(recv, d, "sparse", ws, q_out=qf),
+        "attend_after_fused": lambda: sa.solattn_attend_ws(qf, None, None, outf, prefix_len, tau,
+                                                           "sparse", ws),
+    }
     ms = {}
-    for name, fn in t.items():
+    for name, fn in list(t.items()) + list(fused.items()):
         fn()
         ms[name] = float(np.median(time_calls(fn, 20, stream)))
     nbytes = {"pack_qkv_int8": 3 * B * H * Ns * (2 * d + rec),
               "unpack_qkv_int8": 3 * P * B * Hp * Ns * (rec + 2 * d),
               "pack_out_fp8": B * Hp * N * (2 * d + rec),
-              "unpack_out_fp8": P * B * Hp * Ns * (rec + 2 * d)}
+              "unpack_out_fp8": P * B * Hp * Ns * (rec + 2 * d),
+              # records read, q' written, and what the pooling pass writes
+              "fused_unpack_prepare": 3 * P * B * Hp * Ns * rec + B * Hp * N * d * 2
+                                      + B * Hp * ((N + 63) // 64) * 276 * d}
     res = {"workload": "refine, rank 0 of %d: %d heads x %d tokens attended; shards of %d tokens"
                        % (P, Hp, N, Ns), "P": P, "tau": tau}
     for name, v in ms.items():
@@ -414,7 +426,13 @@ def sp_rank_check(sa, stream, q_all, k_all, v_all, prefix_len, tau, P=8):
         if name in nbytes:
             e["GBps"] = round(nbytes[name] / (v * 1e-3) / 1e9, 1)
         res[name] = e
-    res["rank_step_ms_without_all_to_all"] = round(sum(ms.values()), 4)
+    unfused = ("pack_qkv_int8", "unpack_qkv_int8", "attention", "pack_out_fp8", "unpack_out_fp8")
+    fused_step = ("pack_qkv_int8", "fused_unpack_prepare", "attend_after_fused", "pack_out_fp8",
+                  "unpack_out_fp8")
+    res["rank_step_ms_without_all_to_all"] = round(sum(ms[n] for n in unfused), 4)
+    res["rank_step_ms_fused_receive"] = round(sum(ms[n] for n in fused_step), 4)
+    torch.cuda.synchronize()
+    res["fused_receive_out_equal"] = bool(torch.equal(outf, out8))
     # what the INT8 / FP8 round trip changes on these heads
     qb, kb, vb = (x[:, :Hp].contiguous() for x in (q_all, k_all, v_all))
     ob16, wb, _, _ = sa.solattn_forward_debug(qb, kb, vb, None, prefix_len, tau, "sparse",

@@ -57,6 +57,7 @@ _SIGS = {
     "solattn_transport_record_bytes": ([_I64], _SZ),
     "solattn_pack_qkv_int8": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P], _I),
     "solattn_unpack_qkv_int8": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I),
+    "solattn_prepare_int8_ws": ([_P, _I64, _I64, _I64, _I64, _I64, _I, _P, _P, _SZ, _P], _I),
     "solattn_pack_out_fp8": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _P], _I),
     "solattn_unpack_out_fp8": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _P], _I),
     "solattn_qknorm_rope": ([_P, _P, _P, _P, _F, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I,
@@ -372,6 +373,23 @@ def solattn_unpack_qkv_int8(recv, d: int, q=None, k=None, v=None, stream=None):
     _check(_lib.solattn_unpack_qkv_int8(_ptr(recv), B, Hp, Ns, int(d), P, _ptr(q), _ptr(k), _ptr(v),
                                         _stream(stream)))
     return q, k, v
+
+
+def solattn_prepare_int8_ws(recv, d: int, mode, ws, q_out=None, stream=None):
+    """Received INT8 records [P][B][Hp][Ns][3][rec] -> q_out [B][Hp][P*Ns][d]
+    bf16 and the workspace of the unpacked Q/K/V (dequantize + pool in one
+    pass).  Returns q_out."""
+    import torch
+    _on_gpu(recv, "recv")
+    P, B, Hp, Ns = (int(x) for x in recv.shape[:4])
+    if q_out is None:
+        q_out = torch.empty((B, Hp, P * Ns, d), dtype=torch.bfloat16, device=recv.device)
+    _same_device(recv, q_out, "q_out")
+    _same_device(recv, ws, "ws")
+    _check(_lib.solattn_prepare_int8_ws(_ptr(recv), B, Hp, Ns, int(d), P, _mode_code(mode),
+                                        _ptr(q_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(stream)))
+    return q_out
 
 
 def solattn_pack_out_fp8(o, P: int, send=None, stream=None):

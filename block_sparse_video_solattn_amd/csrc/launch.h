@@ -121,6 +121,18 @@ hipError_t launch_unpack_qkv_int8(const QkvUnpackArgs& a, int d, hipStream_t s);
 hipError_t launch_pack_out_fp8(const OutPackArgs& a, int d, hipStream_t s);
 hipError_t launch_unpack_out_fp8(const OutUnpackArgs& a, int d, hipStream_t s);
 
+// Pooling straight from received INT8 Q/K/V records (transport layout
+// [P][B][Hp][Ns][3][rec]; the slice bh = b * Hp + hp covers N = P * Ns
+// tokens): the rows are dequantized in registers as the unpack kernel
+// dequantizes them, Q rows are written to q_out, and the workspace of a is
+// filled as pool_kernel fills it from the unpacked tensors (bf16 only).
+struct UnpackPoolArgs {
+    const uint8_t* recv;
+    void* q_out;
+    int64_t B, Hp, Ns, P;
+};
+hipError_t launch_unpack_pool(const PoolArgs& a, const UnpackPoolArgs& u, hipStream_t s);
+
 hipError_t launch_pool(const PoolArgs& a, int64_t BH, hipStream_t s);
 hipError_t launch_route(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);

@@ -209,6 +209,131 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Pooling from received INT8 records: the receive side of the sequence-
+// parallel exchange (page "MiniMax 官宣 NVIDIA Sol 团队 H3 加速:5 秒视频 1.653
+// 秒生成并开源", section "提速来自流水线每一段的叠加", multi-GPU item: INT8
+// Q/K/V; page "英伟达开源 Sol-H3，给 MiniMax-H3 加速，5 秒视频 1.4 秒出",
+// section "2.2 剩下三层加速": 144-byte records) fused with step 1, so that
+// the dequantized K and V never reach device memory as bf16 rows.  A thread
+// takes the same 16-byte chunk of the same rows as pool_kernel<bf16, D>:
+// 8 codes (one 8-byte load) and the record's scale, code * s in fp32
+// rounded to bf16 -- the unpack kernel's arithmetic -- then sums, means and
+// operand-ordered tiles exactly as pool_kernel computes them from loaded
+// rows, so the workspace is bit for bit what unpacking and then pooling
+// leaves.  Q rows also go to q_out (the attention reads its queries from
+// there); in dense mode only q_out and the key and value tiles are written.
+template <int D>
+__device__ inline bf16x8 decode_chunk(const UnpackPoolArgs& u, int64_t bh, int64_t N,
+                                      int64_t tok, int which, int c) {
+    constexpr int REC = (D + 4 + 15) / 16 * 16;
+    const int64_t src = tok / u.Ns, t = tok % u.Ns;
+    const int64_t b = bh / u.Hp, hp = bh % u.Hp;
+    const uint8_t* in = u.recv + ((((src * u.B + b) * u.Hp + hp) * u.Ns + t) * 3 + which) * REC;
+    const uint2 w = *reinterpret_cast<const uint2*>(in + c * 8);
+    const float sc = *reinterpret_cast<const float*>(in + D);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t word = e < 4 ? w.x : w.y;
+        const int code = (int)(int8_t)((word >> (8 * (e & 3))) & 0xffu);
+        o[e] = to_bf16((float)code * sc);
+    }
+    return o;
+}
+
+template <int D>
+__device__ inline void decode_rows(const UnpackPoolArgs& u, int64_t bh, int64_t N, int64_t tok0,
+                                   int which, int n, int tid, float (&acc)[8], bf16x8* keep,
+                                   bf16* q_out) {
+    constexpr int CPR = D / 8, RPP = 256 / CPR, PASSES = 64 / RPP;
+    const int c = tid % CPR, r0 = tid / CPR;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int r = r0 + p * RPP;
+        bf16x8 x;
+        if (r < n) {
+            x = decode_chunk<D>(u, bh, N, tok0 + r, which, c);
+            if (q_out) *reinterpret_cast<bf16x8*>(q_out + (bh * N + tok0 + r) * D + c * 8) = x;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (bf16)0.f;
+        }
+        if (keep) keep[p] = x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += (float)x[e];
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void unpack_pool_kernel(PoolArgs a, UnpackPoolArgs u) {
+    constexpr int CPR = D / 8;
+    constexpr int RPP = 256 / CPR;
+    constexpr int PASSES = 64 / RPP;
+    __shared__ float red[RPP * D];
+    __shared__ float mean[D];
+    __shared__ bf16 tile[64][D + 8];
+
+    const int tid = threadIdx.x;
+    const int64_t j = blockIdx.x, bh = blockIdx.y;
+    const int64_t Nb = a.Nb, Nbp = a.Nbp, N = a.N;
+    const int kk = (int)(j & 63);
+    bf16* kbarP = reinterpret_cast<bf16*>(a.kbarP) + (bh * (Nbp / 64) + j / 64) * D * 64;
+    bf16* vbarP = reinterpret_cast<bf16*>(a.vbarP) + (bh * (Nbp / 64) + j / 64) * D * 64;
+    if (j >= Nb) {
+        // padding of the pooled tiles (sparse and top-k modes only)
+        if (!a.pooled) return;
+        if (tid < D) {
+            a.kbarT[(bh * D + tid) * Nbp + j] = 0.f;
+            put_pooled_kv<D>(kbarP, vbarP, kk, tid, 0.f, 0.f);
+        }
+        return;
+    }
+    const int n = (int)((j + 1) * 64 <= N ? 64 : N - j * 64);
+    const int64_t tok0 = j * 64;
+    float acc[8];
+    bf16x8 keep[PASSES];
+    auto stage = [&]() {
+        const int c = tid % CPR, r0 = tid / CPR;
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tile[r0 + p * RPP][c * 8 + e] = keep[p][e];
+    };
+    decode_rows<D>(u, bh, N, tok0, 0, n, tid, acc, nullptr, reinterpret_cast<bf16*>(u.q_out));
+    if (a.pooled) {
+        reduce_mean<bf16, D>(acc, n, tid, red, mean);
+        if (tid < D) a.qbar[(bh * Nb + j) * D + tid] = mean[tid];
+    }
+    decode_rows<D>(u, bh, N, tok0, 1, n, tid, acc, keep, nullptr);
+    if (a.pooled) {
+        reduce_mean<bf16, D>(acc, n, tid, red, mean);
+        if (tid < D) {
+            a.kbar[(bh * Nb + j) * D + tid] = mean[tid];
+            a.kbarT[(bh * D + tid) * Nbp + j] = mean[tid];
+        }
+    }
+    stage();
+    __syncthreads();
+    write_key_tile<D>(tile, reinterpret_cast<bf16*>(a.kP) + (bh * Nb + j) * (int64_t)D * 64, tid);
+    __syncthreads();
+    decode_rows<D>(u, bh, N, tok0, 2, n, tid, acc, keep, nullptr);
+    if (a.pooled) {
+        const float km = tid < D ? mean[tid] : 0.f;  // K mean, still in LDS
+        __syncthreads();
+        reduce_mean<bf16, D>(acc, n, tid, red, mean);
+        if (tid < D) {
+            a.vbar[(bh * Nb + j) * D + tid] = mean[tid];
+            put_pooled_kv<D>(kbarP, vbarP, kk, tid, km, mean[tid]);
+        }
+    }
+    stage();
+    __syncthreads();
+    write_value_tile<D>(tile, reinterpret_cast<bf16*>(a.vP) + (bh * Nb + j) * (int64_t)D * 64, tid);
+}
+
+// ---------------------------------------------------------------------------
 // Fused Q/K producer: QKNorm then partial RoPE on each Q and K row, the
 // results stored in the input's element type, and the block pooling of the
 // same workgroup taken from those stored values (page "MiniMax 官宣 NVIDIA Sol
@@ -518,6 +643,16 @@ hipError_t launch_pool_heads(const PoolArgs& a, int64_t BH, hipStream_t s) {
         else
             hipLaunchKernelGGL((pool_kernel<float, 64>), grid, dim3(256), 0, s, a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack_pool(const PoolArgs& a, const UnpackPoolArgs& u, hipStream_t s) {
+    // (the caller keeps B * Hp within the grid's y limit)
+    const dim3 grid((unsigned)(a.pooled ? a.Nbp : a.Nb), (unsigned)(u.B * u.Hp));
+    if (a.d == 128)
+        hipLaunchKernelGGL((unpack_pool_kernel<128>), grid, dim3(256), 0, s, a, u);
+    else
+        hipLaunchKernelGGL((unpack_pool_kernel<64>), grid, dim3(256), 0, s, a, u);
     return hipGetLastError();
 }
 

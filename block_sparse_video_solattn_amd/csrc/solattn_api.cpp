@@ -650,6 +650,34 @@ int solattn_unpack_qkv_int8(const void* recv, int64_t B, int64_t Hp, int64_t Ns,
     return e == hipSuccess ? SOLATTN_OK : hip_fail(e, "unpack kernel launch");
 }
 
+int solattn_prepare_int8_ws(const void* recv, int64_t B, int64_t Hp, int64_t Ns, int64_t d,
+                            int64_t P, int mode, void* q_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+    g_last_error.clear();
+    int rc = check_transport(B, Hp, Ns, d, P);
+    if (rc) return rc;
+    const int64_t N = P * Ns;
+    // shapes, mode and alignment as for solattn_prepare_ws on the unpacked
+    // tensors (q_out stands in for q, k and v)
+    if ((rc = validate(q_out, q_out, q_out, nullptr, false, B, Hp, N, d, 0, 0.f, mode,
+                       SOLATTN_BF16)))
+        return rc;
+    if (B * Hp > 65535)
+        return fail(SOLATTN_EUNSUPPORTED, "B*Hp = %lld exceeds 65535 slices", (long long)(B * Hp));
+    if ((rc = check_ws(ws, ws_bytes, B, Hp, N, d, SOLATTN_BF16))) return rc;
+    const size_t rb = (size_t)P * B * Hp * Ns * 3 * solattn_transport_record_bytes(d),
+                 tb = (size_t)B * Hp * N * d * 2;
+    if ((rc = check_buffers({recv}, rb, {q_out}, tb))) return rc;
+    if (overlaps(ws, ws_bytes, recv, rb) || overlaps(ws, ws_bytes, q_out, tb))
+        return fail(SOLATTN_EINVAL, "ws must not overlap recv or q_out");
+    if ((rc = check_device_ptrs({recv, q_out, ws}))) return rc;
+    const PoolArgs p = pool_args(nullptr, nullptr, nullptr, B, Hp, N, d, mode, SOLATTN_BF16, ws,
+                                 true);
+    UnpackPoolArgs u{static_cast<const uint8_t*>(recv), q_out, B, Hp, Ns, P};
+    const hipError_t e = launch_unpack_pool(p, u, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOLATTN_OK : hip_fail(e, "unpack-pool kernel launch");
+}
+
 int solattn_pack_out_fp8(const void* o, int64_t B, int64_t Hp, int64_t Ns, int64_t d, int64_t P,
                          void* send, void* stream) {
     g_last_error.clear();

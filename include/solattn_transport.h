@@ -61,6 +61,22 @@ int solattn_pack_qkv_int8(const void* q, const void* k, const void* v, int64_t B
 int solattn_unpack_qkv_int8(const void* recv, int64_t B, int64_t Hp, int64_t Ns, int64_t d,
                             int64_t P, void* q, void* k, void* v, void* stream);
 
+/* The receive side fused with step 1 of Sol-Attn: the received INT8 records
+ * (recv as for solattn_unpack_qkv_int8, N = P*Ns tokens per slice) are
+ * dequantized in registers (bf16 of code * s, as solattn_unpack_qkv_int8
+ * computes it) and pooled, so the bf16 K and V rows are never written.
+ * Writes q_out [B][Hp][N][d] bf16 (the queries, as solattn_unpack_qkv_int8
+ * would write q) and fills the workspace ws (ws_bytes >=
+ * solattn_workspace_bytes(B, Hp, N, d, SOLATTN_BF16), 256-byte aligned) bit
+ * for bit as solattn_prepare_ws(q, k, v, B, Hp, N, d, mode, SOLATTN_BF16)
+ * would from the unpacked tensors.  solattn_attend_ws(q_out, NULL, NULL, ...)
+ * then completes the attention (the bf16 kernel reads keys and values from
+ * the workspace only).  mode: as for solattn_prepare_ws (include/solattn.h).
+ * B*Hp <= 65535; recv, q_out and ws must not overlap.  Allocates nothing. */
+int solattn_prepare_int8_ws(const void* recv, int64_t B, int64_t Hp, int64_t Ns, int64_t d,
+                            int64_t P, int mode, void* q_out, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /* Attention output of this rank's heads -> per-destination FP8 records.
  *   o:    [B][Hp][P*Ns][d].
  *   send: [P][B][Hp][Ns][rec]; chunk r holds tokens r*Ns .. r*Ns + Ns - 1. */

@@ -170,3 +170,50 @@ def test_transport_at_the_benchmark_shape():
     oback = sa.solattn_unpack_out_fp8(torch.from_numpy(orecv).cuda(), d)
     torch.cuda.synchronize()
     assert np.array_equal(to_np_bf16(oback).view(np.uint32), T.unpack_out_fp8(orecv, d).view(np.uint32))
+
+
+@pytest.mark.parametrize("P,B,Hp,Ns,d,mode", [
+    (2, 1, 2, 100, 128, "sparse"),      # blocks straddle the two sequence shards, ragged tail
+    (3, 2, 1, 64, 64, "sparse"),
+    (4, 1, 2, 96, 128, "dense"),
+    (2, 1, 3, 130, 128, "topk"),
+    (8, 1, 4, 2048, 128, "sparse"),     # one rank of 8 at the refine shape
+])
+def test_fused_unpack_prepare_matches_unpack_then_prepare(P, B, Hp, Ns, d, mode):
+    # the receive side fused with pooling: q_out and the whole workspace bit
+    # for bit as unpacking then solattn_prepare_ws, and the attention on them
+    # equal to the forward call on the unpacked tensors
+    import torch
+    import block_sparse_video_solattn_amd as sa
+    from block_sparse_video_solattn_amd import inputs
+    N = P * Ns
+    rng = np.random.default_rng(P * 1000 + Ns)
+    if Ns >= 1024:
+        grid = (-(-(N - 128) // (24 * 42)), 24, 42)
+        q, k, v = inputs.custom(B, P * Hp, Ns, d, "bf16", seed=17)   # this rank's shard, all heads
+        shard = [to_dev(x) for x in (q, k, v)]
+        send = sa.solattn_pack_qkv_int8(*shard, P)
+        recv = torch.stack([send[0]] * P).contiguous()   # every chunk from "rank 0"'s shard
+    else:
+        recs = []
+        for _ in range(P):
+            q, k, v = (bf16_values(rng, (B, P * Hp, Ns, d)) for _ in range(3))
+            recs.append(sa.solattn_pack_qkv_int8(to_dev(q), to_dev(k), to_dev(v), P)[0])
+        recv = torch.stack(recs).contiguous()
+    torch.cuda.synchronize()
+    wsb = sa.solattn_workspace_bytes(B, Hp, N, d, sa.BF16)
+    ws0 = torch.zeros(wsb, dtype=torch.uint8, device="cuda")    # (alignment gaps stay zero)
+    ws1 = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    qu, ku, vu = sa.solattn_unpack_qkv_int8(recv, d)
+    sa.solattn_prepare_ws(qu, ku, vu, mode, ws0)
+    q1 = sa.solattn_prepare_int8_ws(recv, d, mode, ws1)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, qu)
+    assert torch.equal(ws1, ws0)
+    tau = {"sparse": 1.25, "dense": 0.0, "topk": 0.2}[mode]
+    o0, o1 = torch.empty_like(qu), torch.empty_like(qu)
+    sa.solattn_attend_ws(qu, ku, vu, o0, 0, tau, mode, ws0)
+    sa.solattn_attend_ws(q1, None, None, o1, 0, tau, mode, ws1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1.float()).all()
+    assert torch.equal(o1, o0)
