@@ -1,12 +1,18 @@
-"""Calibrate tau for the draft-stage workload (672x384 latent geometry,
-32 heads x 32768 tokens, prefix 512) so that ~90 % of the (query block,
-video key block) pairs are skipped: the draft stage runs its sparse
-attention at 90 % video sparsity with 64-token blocks (page "NVIDIA 团队开源
-Sol-H3 的 DGX Spark 版本", section "潜空间直传").
+"""Calibrate tau so that ~90 % of the (query block, video key block) pairs
+are skipped.
+
+* draft (default): the draft-stage workload (672x384 latent geometry, 32
+  heads x 32768 tokens, prefix 512), which runs its sparse attention at 90 %
+  video sparsity with 64-token blocks (page "NVIDIA 团队开源 Sol-H3 的 DGX
+  Spark 版本", section "潜空间直传"); writes draft_tau.json.
+* refine: the refine-stage workload at the seed the benchmark uses, so that
+  its speed-up over dense attention can also be read at exactly ~90 % video
+  sparsity next to the tau values the refine steps use (1.0 / 1.25 / 1.5);
+  writes refine_tau90.json.
 
 Uses only the oracle's routing (scores and masks in fp64) on the seeded
-inputs; writes draft_tau.json next to this script.
-Usage: python tests/golden/make_draft_tau.py
+inputs; writes the JSON next to this script.
+Usage: python tests/golden/make_draft_tau.py [draft|refine]
 """
 import json
 import os
@@ -21,7 +27,8 @@ import numpy as np  # noqa: E402
 import oracle  # noqa: E402
 from block_sparse_video_solattn_amd import inputs  # noqa: E402
 
-SEED = 4000
+SEEDS = {"draft": 4000, "refine": 3000}   # the seeds the benchmark generates them with
+FILES = {"draft": "draft_tau.json", "refine": "refine_tau90.json"}
 TARGET = (0.895, 0.905)
 
 
@@ -35,9 +42,10 @@ def video_skip_fraction(q, k, v, w, tau):
     return skipped / total
 
 
-def main():
-    w = inputs.WORKLOADS["draft"]
-    q, k, v = inputs.make_inputs(w, SEED)
+def main(name="draft"):
+    w = inputs.WORKLOADS[name]
+    seed = SEEDS[name]
+    q, k, v = inputs.make_inputs(w, seed)
     lo, hi = 0.0, 4.0
     tau = 2.0
     for it in range(30):
@@ -50,15 +58,15 @@ def main():
             lo = tau
         else:
             hi = tau
-    out = {"workload": "draft", "seed": SEED, "tau": round(tau, 6), "video_skip_fraction": f,
+    out = {"workload": name, "seed": seed, "tau": round(tau, 6), "video_skip_fraction": f,
            "target": list(TARGET),
            "note": "tau chosen by bisection on [0, 4] with the oracle's routing; the draft "
                    "stage's 90% video sparsity is from page 'NVIDIA 团队开源 Sol-H3 的 DGX Spark "
                    "版本', section '潜空间直传'"}
-    with open(os.path.join(HERE, "draft_tau.json"), "w") as fh:
+    with open(os.path.join(HERE, FILES[name]), "w") as fh:
         json.dump(out, fh, indent=1)
     print(out)
 
 
 if __name__ == "__main__":
-    main()
+    main(sys.argv[1] if len(sys.argv) > 1 else "draft")

@@ -103,6 +103,16 @@ def test_refine_workload(tau):
     run_workload("refine", 3000, tau, heads=(0, 13, 31), block_step=8)
 
 
+def test_refine_workload_tau_at_90_percent():
+    # refine at the tau the oracle's routing puts at ~90 % video sparsity
+    # (tests/golden/refine_tau90.json), where the dense speed-up is also read
+    with open(os.path.join(GOLDEN, "refine_tau90.json")) as f:
+        cal = json.load(f)
+    m = run_workload("refine", cal["seed"], cal["tau"], heads=(0, 31), block_step=8)
+    pb = 4
+    assert abs((1 - m[..., pb:].mean()) - 0.90) < 0.01
+
+
 def test_draft_workload_calibrated_tau():
     with open(os.path.join(GOLDEN, "draft_tau.json")) as f:
         cal = json.load(f)
