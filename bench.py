@@ -740,6 +740,18 @@ def main():
         res["speedup_vs_dense"] = round(dms / ms_per_step, 2)
         # like for like: both medians of HIP-event-timed calls
         res["speedup_vs_dense_event_median"] = round(dms / float(np.median(call_list)), 2)
+        # and in the same thermal state: dense and sparse calls alternated,
+        # each timed by its own events (the part's clock drifts by ~5 %
+        # between a run of dense calls and a run of sparse ones)
+        def sparse_call():
+            sa.solattn_forward_ws(qd, kd, vd, out, w.prefix_len, tau, "sparse", ws)
+        alt_d, alt_s = [], []
+        for _ in range(12):
+            alt_d += time_calls(dense, 1, stream)
+            alt_s += time_calls(sparse_call, 1, stream)
+        res["alternating_dense_sparse_ms"] = [round(float(np.median(alt_d)), 4),
+                                              round(float(np.median(alt_s)), 4)]
+        res["speedup_vs_dense_alternating"] = round(float(np.median(alt_d)) / float(np.median(alt_s)), 2)
         sweep = {}
         for t in w.taus:
             def sp(t=t):
