@@ -89,8 +89,6 @@ int validate(const void* q, const void* k, const void* v, const void* out, bool 
                     (long long)N, (long long)kMaxN);
     if (B > (int64_t(1) << 40) / H || B * H > (int64_t(1) << 31) / ((N + 63) / 64))
         return fail(SOLATTN_EUNSUPPORTED, "B*H*ceil(N/64) exceeds 2^31 workgroups");
-    if (B * H > 65535)   // the pooling grid has one row (gridDim.y) per (batch, head) slice
-        return fail(SOLATTN_EUNSUPPORTED, "B*H = %lld exceeds 65535 slices", (long long)(B * H));
     if (out) {
         const size_t bytes = (size_t)B * H * N * d * (dtype == SOLATTN_BF16 ? 2 : 4);
         if (overlaps(out, bytes, q, bytes) || (k && overlaps(out, bytes, k, bytes)) ||

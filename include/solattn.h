@@ -32,8 +32,7 @@
  *   - q, k, v, out: caller-owned device pointers to contiguous row-major
  *     [B][H][N][d] tensors, all of element type `dtype`, 16-byte aligned.
  *     Inputs are read only; `out` must not overlap any input.
- *   - B, H, N >= 1; d is 64 or 128; 0 <= prefix_len <= N; N <= 262144;
- *     B*H <= 65535 (SOLATTN_EUNSUPPORTED beyond: one grid row per slice).
+ *   - B, H, N >= 1; d is 64 or 128; 0 <= prefix_len <= N; N <= 262144.
  *   - tau may be +-infinity; NaN is rejected.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *     work on it and return without synchronising; completion is observed

@@ -69,7 +69,7 @@ def fwd(lib, q=A, k=A + 0x100000, v=A + 0x200000, out=A + 0x300000, B=1, H=1, N=
     (dict(mode=2, tau=0.0), 1), (dict(mode=2, tau=1.5), 1), (dict(mode=2, tau=-math.inf), 1),
     (dict(mode=0x10), 1), (dict(mode=0x20), 1), (dict(mode=0x22, tau=0.5), 1), (dict(mode=0x81), 1),
     (dict(mode=0x40), 1), (dict(mode=0x42, tau=0.5), 1), (dict(mode=0x41, dtype=0), 2),
-    (dict(mode=0x13, tau=0.5), 1), (dict(N=64 * 4096 + 1), 2), (dict(B=2, H=32768, N=64), 2),
+    (dict(mode=0x13, tau=0.5), 1), (dict(N=64 * 4096 + 1), 2),
 ])
 def test_forward_rejects_before_device(lib, kw, code):
     assert fwd(lib, **kw) == code
