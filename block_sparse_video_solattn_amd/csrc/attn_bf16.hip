@@ -117,6 +117,22 @@ __device__ __forceinline__ void acc_fence() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// The fast path's accumulators copied out of the accumulation registers
+// by asm of its own, after acc_fence (volatile asm keeps its order): with
+// every later use an asm operand in accumulation registers, the compiler
+// has no reason to place copies of its own -- which could land between the
+// last MFMA and the fence -- on the way out of the loop.
+template <int D>
+__device__ __forceinline__ void acc_read(const f32x16 (&acc)[D / 32][2], f32x16 (&out)[D / 32][2]) {
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(out[mt][nt][v]) : "a"(acc[mt][nt][v]));
+}
+
 // max(x, x of lane ^ 32) without an LDS round trip: v_permlane32_swap
 // exchanges the upper 32 lanes of one copy with the lower 32 lanes of the
 // other, so each lane ends up holding both values.
@@ -780,7 +796,11 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
         abandoned = abandoned ||
                     __ballot(!(fs.lsum[0] <= kFixedSumMax && fs.lsum[1] <= kFixedSumMax)) != 0;
         acc_fence();
-        if (!abandoned) store_rows<D>(fs.oacc, fs.lsum, op, i, N, half, l32);
+        if (!abandoned) {
+            f32x16 o[MT][2];
+            acc_read<D>(fs.oacc, o);
+            store_rows<D>(o, fs.lsum, op, i, N, half, l32);
+        }
     }
     if (!abandoned) return;
 
