@@ -31,3 +31,28 @@ def test_legs_listed_in_help():
     text = "".join(r.stdout.split())      # argparse wraps the list where it likes
     for leg in ("mfma_probe", "dense_sweep", "torch_sdpa", "taylor1", "qk_producer", "long_clip"):
         assert leg in text
+
+
+def test_traffic_constants_follow_the_committed_counter_summary():
+    # roofline.traffic comes from the FETCH_SIZE / WRITE_SIZE figures of the
+    # committed counter summary: the constants bench.py keeps must be that
+    # summary's numbers and hash; with the attention sources as they stand
+    # the bench reports that traffic, and once they change it reports null
+    # (until the counters are taken again)
+    import re
+    sys.path.insert(0, ROOT)
+    import bench
+    c = bench.ATTN_COUNTERS
+    with open(os.path.join(ROOT, c["profile"])) as f:
+        text = f.read()
+    m = re.search(r"roofline\.traffic = \(([\d.]+) x ([\d.]+) \+ ([\d.]+)\) x 1024 = (\d+) bytes",
+                  text)
+    assert m, "no roofline.traffic line in the summary"
+    fetch, fscale, write, total = float(m.group(1)), float(m.group(2)), float(m.group(3)), int(m.group(4))
+    assert (fetch, fscale, write) == (c["fetch_kib"], c["fetch_scale"], c["write_kib"])
+    assert round((fetch * fscale + write * c["write_scale"]) * 1024) == total
+    assert c["sources_sha256"] in "".join(text.split())
+    if bench.attn_sources_sha256() == c["sources_sha256"]:
+        assert bench.attn_traffic_bytes() == total
+    else:
+        assert bench.attn_traffic_bytes() is None
