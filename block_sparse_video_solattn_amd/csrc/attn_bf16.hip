@@ -618,6 +618,28 @@ __device__ __attribute__((noinline)) void attend_taylor(
                             klist, plist, slist, n_skip);
 }
 
+// Work item of workgroup g: xcd_remap's contiguous (head, query block) range
+// per XCD, in order -- except that with dense prefix rows the prefix query
+// blocks of the range (i < Pb: every key block exact, ~7x a routed block's
+// work at the refine shape) come first, so that the dispatch does not end
+// on them.
+__device__ inline int64_t work_order(int64_t g, int64_t T, int64_t Nb, int64_t Pb,
+                                     bool heavy_first) {
+    const int64_t x = g % 8, r = g / 8, q = T / 8, m = T % 8;
+    const int64_t start = x * q + (x < m ? x : m);
+    if (!heavy_first || Pb < 1 || Pb >= Nb) return start + r;   // = xcd_remap(g, T)
+    const int64_t nbx = q + (x < m ? 1 : 0);
+    // prefix items (block index < Pb) among the first n items, head-major
+    auto P = [&](int64_t n) { return n / Nb * Pb + (n % Nb < Pb ? n % Nb : Pb); };
+    const int64_t p0 = P(start), npx = P(start + nbx) - p0;
+    if (r < npx) {
+        const int64_t k = p0 + r;                 // the k-th prefix item
+        return k / Pb * Nb + k % Pb;
+    }
+    const int64_t k = (start - p0) + (r - npx);   // the k-th other item
+    return k / (Nb - Pb) * Nb + Pb + k % (Nb - Pb);
+}
+
 template <int D>
 __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     constexpr int KS = D / 16;  // k-steps of S^T = K Q^T
@@ -626,7 +648,8 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
 
     const int lane = threadIdx.x, half = lane >> 5, l32 = lane & 31;
     const int64_t N = a.N, Nb = a.Nb, Nbp = a.Nbp;
-    const int64_t w = xcd_remap(blockIdx.x, a.BH * Nb);
+    const int64_t w = work_order(blockIdx.x, a.BH * Nb, Nb, a.Pb,
+                                 a.mode != kDense && a.prefix_rows);
     const int64_t bh = w / Nb, i = w % Nb;
     // LDS: srow[Nbp] routing scores, then pooled-key biases; two 64-entry
     // bias rows for exact tiles (all zero; zero then -inf past the tail
