@@ -728,8 +728,10 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
 
     // Fast path.  Phases (sched barriers keep them, and so the order of the
     // loads that the in-order vmcnt waits rely on, in place):
+    //   loads of the values of half h+1 (into the buffer that the PV
+    //   product of half h-1 has just read);
     //   S^T of half h+1 beside the exp2 work of half h;
-    //   loads of the values of half h+1, then of the keys of half h+3;
+    //   loads of the keys of half h+3 (into the buffer S^T has just read);
     //   PV of half h with the logits (scale and bias) of half h+1 placed
     //   between its MFMAs by hand (pv_then_head).
     // Past the end the prefetches and the S^T products re-read the last tile
@@ -783,27 +785,29 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        // Values are loaded one phase pair ahead of their PV product, keys
-        // two (each key buffer is refilled right after its S^T product), and
-        // each value load is issued before the key load of the same phase so
-        // that waiting for the values does not wait for the keys.
+        // Each buffer is refilled as soon as the product that reads it has
+        // issued: values two S^T phases and one PV phase ahead of their PV
+        // product, keys two PV phases and one S^T phase ahead of their S^T
+        // product.  The loads go out in the order of their use (V(h),
+        // K(h+2), V(h+1), K(h+3), ...), so waiting for one operand never
+        // waits for a later one.
         for (int t = 0; t < n_tiles && !abandoned; ++t) {
             const TileRef t2 = t + 2 < n_tiles ? tile_at(t + 2) : t1;
+            load_v<D>(t0, 1, lane, vB1);
+            __builtin_amdgcn_sched_barrier(0);
             s_product_from<D>(kB1, qB, cinit, st1);          // S^T (t, 1)
             softmax_tail_rel(st0, fs, pB);                   // exp2 (t, 0)
             interleave<16, 6>();
-            __builtin_amdgcn_sched_barrier(0);
-            load_v<D>(t0, 1, lane, vB1);
             __builtin_amdgcn_sched_barrier(0);
             load_k<D>(t1, 1, lane, kB1);
             __builtin_amdgcn_sched_barrier(0);
             pv_then_head<D>(vB0, pB, fs, st1, t0, 1, srow, half, scale2);  // PV (t, 0)
             __builtin_amdgcn_sched_barrier(0);
+            load_v<D>(t1, 0, lane, vB0);
+            __builtin_amdgcn_sched_barrier(0);
             s_product_from<D>(kB0, qB, cinit, st0);          // S^T (t+1, 0)
             softmax_tail_rel(st1, fs, pB);                   // exp2 (t, 1)
             interleave<16, 6>();
-            __builtin_amdgcn_sched_barrier(0);
-            load_v<D>(t1, 0, lane, vB0);
             __builtin_amdgcn_sched_barrier(0);
             load_k<D>(t2, 0, lane, kB0);
             __builtin_amdgcn_sched_barrier(0);
