@@ -46,15 +46,36 @@ __device__ inline float kth_largest_video(const float* srow, int64_t Pb, int64_t
     if (k < 1) return __builtin_inff();
     const int lane = threadIdx.x & 63;
     uint32_t key = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = key | (1u << bit);
-        int64_t count = 0;
-        for (int64_t j0 = 0; j0 < Nb; j0 += 64) {
-            const int64_t j = j0 + lane;
-            const bool ge = j >= Pb && j < Nb && order_key(srow[j]) >= cand;
-            count += __popcll(__ballot(ge));
+    // Rows of up to 64 * R blocks keep their keys in registers for the 32
+    // rounds (a video column's key, or 0 -- which no candidate reaches, every
+    // candidate having a bit set -- elsewhere); longer rows re-read the LDS.
+    constexpr int R = 16;
+    if (Nb <= 64 * R) {
+        uint32_t kr[R];
+#pragma unroll
+        for (int c = 0; c < R; ++c) {
+            const int64_t j = 64 * c + lane;
+            kr[c] = (j >= Pb && j < Nb) ? order_key(srow[j]) : 0u;
         }
-        if (count >= k) key = cand;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = key | (1u << bit);
+            int64_t count = 0;
+#pragma unroll
+            for (int c = 0; c < R; ++c)
+                if (64 * c < Nb) count += __popcll(__ballot(kr[c] >= cand));
+            if (count >= k) key = cand;
+        }
+    } else {
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = key | (1u << bit);
+            int64_t count = 0;
+            for (int64_t j0 = 0; j0 < Nb; j0 += 64) {
+                const int64_t j = j0 + lane;
+                const bool ge = j >= Pb && j < Nb && order_key(srow[j]) >= cand;
+                count += __popcll(__ballot(ge));
+            }
+            if (count >= k) key = cand;
+        }
     }
     const uint32_t b = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
     return __uint_as_float(b);
