@@ -18,8 +18,10 @@
 //     pipeline whose phases pair matrix-core and vector work: the S^T
 //     products of half h+1 run beside the exp2 work of half h, and the PV
 //     products of half h beside the logits of half h+1, with the MFMAs and
-//     vector instructions interleaved one by one.  Keys are prefetched into
-//     registers two halves ahead, values one half ahead;
+//     vector instructions interleaved one by one.  Each key or value
+//     register buffer is refilled as soon as the product that reads it has
+//     issued (keys about two halves ahead of use, values about one and a
+//     half);
 //   * one wave per SIMD: the 64 x d fp32 output accumulator and the value
 //     buffers live in the accumulation VGPRs (the PV MFMAs are inline asm),
 //     the arch VGPRs hold Q^T, S^T, P and the key buffers;
