@@ -76,8 +76,21 @@ def kept_flops(mask, N, d):
     return fk, fp
 
 
-def time_calls(fn, n, stream):
+# GPU time of untimed calls run before every timed series: after an idle gap
+# (a host synchronisation, work on the CPU) the part's clocks take about this
+# long to come back up, so a series timed at once would mix ramp-up calls in
+SETTLE_MS = 30.0
+
+
+def time_calls(fn, n, stream, settle_ms=SETTLE_MS):
+    """HIP-event times (ms) of n back-to-back calls of fn on `stream`, after
+    untimed calls worth about settle_ms of GPU time (at least two)."""
+    import math
     import torch
+    if settle_ms > 0:
+        one = time_calls(fn, 1, stream, settle_ms=0)[0]
+        for _ in range(max(2, int(math.ceil(settle_ms / max(one, 1e-3))))):
+            fn()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
     evs[0].record(stream)
     for i in range(n):
@@ -746,9 +759,12 @@ def main():
         def sparse_call():
             sa.solattn_forward_ws(qd, kd, vd, out, w.prefix_len, tau, "sparse", ws)
         alt_d, alt_s = [], []
+        for _ in range(4):
+            dense()
+            sparse_call()
         for _ in range(12):
-            alt_d += time_calls(dense, 1, stream)
-            alt_s += time_calls(sparse_call, 1, stream)
+            alt_d += time_calls(dense, 1, stream, settle_ms=0)
+            alt_s += time_calls(sparse_call, 1, stream, settle_ms=0)
         res["alternating_dense_sparse_ms"] = [round(float(np.median(alt_d)), 4),
                                               round(float(np.median(alt_s)), 4)]
         res["speedup_vs_dense_alternating"] = round(float(np.median(alt_d)) / float(np.median(alt_s)), 2)
