@@ -223,20 +223,21 @@ def draft_check(sa, stream):
 
 
 def route_bytes(B, H, N, d):
-    """Algorithmic bytes of the scoring pass (solattn_route_ws without
-    exports): the fp32 pooled queries and the transposed pooled keys, read
-    once (B*H*Nb*d*4 + B*H*d*Nbp*4); nothing is written."""
+    """Algorithmic bytes of the bf16 scoring pass (solattn_route_ws without
+    exports): the query rows, from which each query block's mean is formed,
+    and the transposed pooled keys, read once (B*H*N*d*2 + B*H*d*Nbp*4);
+    nothing is written."""
     nb = (N + 63) // 64
     nbp = (nb + 63) // 64 * 64
-    return B * H * nb * d * 4 + B * H * d * nbp * 4
+    return B * H * N * d * 2 + B * H * d * nbp * 4
 
 
 def route_l2_bytes(B, H, N, d):
     """Bytes the scoring pass reads from L2: the transposed pooled keys once
-    per group of four query blocks, plus the pooled queries."""
+    per group of four query blocks."""
     nb = (N + 63) // 64
     nbp = (nb + 63) // 64 * 64
-    return B * H * ((nb + 3) // 4) * d * nbp * 4 + B * H * nb * d * 4
+    return B * H * ((nb + 3) // 4) * d * nbp * 4
 
 
 def scoring_pass(sa, stream, qd, w, tau, ws):
@@ -306,13 +307,14 @@ def small_configs_check(sa, stream):
 
 
 def pool_bytes(B, H, N, d):
-    """Algorithmic HBM bytes of one packing pass of the pooling kernel: per
-    (slice, 64-token block) 3*64*d bf16 elements read; written: the fp32
-    means of q, k and v, the fp32 transposed key mean, the bf16 pooled key
-    and value operands and the bf16 operand-ordered 64 x d key and value
-    tiles (384*d read + 276*d written bytes per block)."""
+    """Algorithmic HBM bytes of one packing pass of the pooling kernel (bf16):
+    per (slice, 64-token block) the 2*64*d bf16 elements of k and v read
+    (the attention kernel forms the query means from the query rows itself);
+    written: the fp32 means of k and v, the fp32 transposed key mean, the
+    bf16 pooled key and value operands and the bf16 operand-ordered 64 x d
+    key and value tiles (256*d read + 272*d written bytes per block)."""
     nb = (N + 63) // 64
-    return B * H * nb * (384 + 276) * d
+    return B * H * nb * (256 + 272) * d
 
 
 def long_clip_check(sa, stream):
@@ -431,7 +433,7 @@ def sp_rank_check(sa, stream, q_all, k_all, v_all, prefix_len, tau, P=8):
               "unpack_out_fp8": P * B * Hp * Ns * (rec + 2 * d),
               # records read, q' written, and what the pooling pass writes
               "fused_unpack_prepare": 3 * P * B * Hp * Ns * rec + B * Hp * N * d * 2
-                                      + B * Hp * ((N + 63) // 64) * 276 * d}
+                                      + B * Hp * ((N + 63) // 64) * 272 * d}
     res = {"workload": "refine, rank 0 of %d: %d heads x %d tokens attended; shards of %d tokens"
                        % (P, Hp, N, Ns), "P": P, "tau": tau}
     for name, v in ms.items():
@@ -524,8 +526,9 @@ def producer_check(sa, stream, tau):
     m = sa.unpack_mask(words, w.nb)
     el = B * H * N * d * 2                       # bytes of one bf16 [B,H,N,d] tensor
     tab = 2 * N * (r // 2) * 4                   # both rotary tables, read once
-    nbytes = {"fused_prepare": pool_bytes(B, H, N, d) + el + tab,
-              "fused_prepare_with_k_out": pool_bytes(B, H, N, d) + 2 * el + tab,
+    # (the fused pass also reads the pre-norm q and writes q')
+    nbytes = {"fused_prepare": pool_bytes(B, H, N, d) + 2 * el + tab,
+              "fused_prepare_with_k_out": pool_bytes(B, H, N, d) + 3 * el + tab,
               "producer_alone": 4 * el + tab,
               "pool_after_producer": pool_bytes(B, H, N, d)}
     res = {"workload": "refine shape from pre-norm Q/K: RMS QKNorm (eps 1e-6, weights) + RoPE "
@@ -688,7 +691,7 @@ def main():
 
     dense_flops = 4.0 * B * H * N * N * d
     attn_tflops = fk / (attn_ms * 1e-3) / 1e12
-    pool_read = 3.0 * B * H * N * d * 2
+    pool_read = 2.0 * B * H * N * d * 2   # k and v
     res = {
         "metric": METRIC,
         "value": round(ms_per_step, 4),

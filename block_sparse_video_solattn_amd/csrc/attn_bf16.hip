@@ -655,7 +655,8 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     const int64_t bh = w / Nb, i = w % Nb;
     // LDS: srow[Nbp] routing scores, then pooled-key biases; two 64-entry
     // bias rows for exact tiles (all zero; zero then -inf past the tail
-    // block's last key); the kept list; the pooled-tile list
+    // block's last key; before that, the block's query mean while the
+    // scores are formed); the kept list; the pooled-tile list
     float* srow = smem;
     const int zero_bias = (int)Nbp, tail_bias = (int)Nbp + 64;
     uint16_t* klist = reinterpret_cast<uint16_t*>(smem + Nbp + 128);
@@ -672,7 +673,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     // query block: lane holds query 32*nt + l32, d = 16*s + 8*half .. +7.
     // Loaded between the two parts of the routing, so that the block's trip
     // from HBM overlaps the threshold and keep-mask work.
-    if (a.mode != kDense) route_scores<D>(a, bh, i, srow);
+    if (a.mode != kDense) route_scores<D, true>(a, bh, i, srow, srow + Nbp);
     bf16x8 qB[2][KS];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -865,7 +866,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_taylor_kernel(AttnArgs a) {
     const bf16* vbp = reinterpret_cast<const bf16*>(a.vbarP) + bh * Nbp * D;
     const int tail = (int)(N - (Nb - 1) * 64);
 
-    route_scores<D>(a, bh, i, srow);
+    route_scores<D, true>(a, bh, i, srow, srow + Nbp);
     const RouteResult r = route_select(a, bh, i, srow, klist);
     srow[zero_bias + lane] = 0.f;
     srow[tail_bias + lane] = lane < tail ? 0.f : -__builtin_inff();

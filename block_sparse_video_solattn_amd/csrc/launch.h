@@ -13,7 +13,8 @@ enum Mode { kDense = 0, kSparse = 1, kTopk = 2 };
 
 // Workspace regions (byte offsets, each 256-byte aligned).  BH = B*H,
 // Nb = ceil(N/64), Nbp = Nb rounded up to a multiple of 64.
-//   qbar, kbar, vbar  fp32 [BH][Nb][d]     block means
+//   qbar, kbar, vbar  fp32 [BH][Nb][d]     block means (qbar: fp32 inputs and the
+//                                          pooled-means export only)
 //   kbarT             fp32 [BH][d][Nbp]    block means of K, transposed for the
 //                                          coalesced score pass; zero padded
 //   kbarP             bf16 [BH][Nbp/64][64*d] pooled keys, MFMA operand order (bf16 only)
@@ -62,6 +63,9 @@ struct PoolArgs {
     int64_t N, Nb, Nbp;
     int d, dtype;
     int pooled;   // compute block means (sparse and topk modes)
+    int qmeans;   // with pooled: the query means too (fp32 inputs, and the
+                  // pooled-means export; the bf16 attention and routing
+                  // kernels form each query block's mean from its rows)
     int pack;     // write the operand-ordered key and value tiles (bf16)
 };
 

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
             for (int e = 0; e < VEC; ++e) tile[r0 + p * RPP][c * VEC + e] = (bf16)keep[p][e];
     };
 
-    if (a.pooled) {
+    if (a.pooled && a.qmeans) {
         load_rows<T, D>(reinterpret_cast<const T*>(a.q) + row0 * D, n, tid, acc, nullptr);
         reduce_mean<T, D>(acc, n, tid, red, mean);
         if (tid < D) a.qbar[(bh * Nb + j) * D + tid] = mean[tid];
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256) void unpack_pool_kernel(PoolArgs a, UnpackPool
             for (int e = 0; e < 8; ++e) tile[r0 + p * RPP][c * 8 + e] = keep[p][e];
     };
     decode_rows<D>(u, bh, N, tok0, 0, n, tid, acc, nullptr, reinterpret_cast<bf16*>(u.q_out));
-    if (a.pooled) {
+    if (a.pooled && a.qmeans) {
         reduce_mean<bf16, D>(acc, n, tid, red, mean);
         if (tid < D) a.qbar[(bh * Nb + j) * D + tid] = mean[tid];
     }
@@ -534,7 +534,7 @@ __global__ __launch_bounds__(256) void produce_pool_kernel(PoolArgs a, ProducerA
                            reinterpret_cast<T*>(pr.q_out) + row0 * D, n, j * 64, tid, prod, acc,
                            nullptr);
     }
-    if (a.pooled) {
+    if (a.pooled && a.qmeans) {
         reduce_mean<T, D>(acc, n, tid, red, mean);
         if (tid < D) a.qbar[(bh * Nb + j) * D + tid] = mean[tid];
     }

@@ -87,20 +87,92 @@ struct RouteResult {
                          // holds at least one skipped block
 };
 
+// Step 1 for the query side of one bf16 query block, done by the wave that
+// routes it: the block's query mean from its rows (the pooling pass then
+// reads no queries).  Lane l takes the 16-byte chunk c = l % CPR of rows
+// g, g + RPI, g + 2 RPI, ... (g = l / CPR); query_rows_load issues those
+// loads, query_rows_mean sums them in fp32 in row order, adds the RPI
+// partial sums of each chunk across lanes (xor butterfly over the row
+// groups; every lane ends with the same sums) and writes sum / n to
+// qm[0..D) in LDS.  Rows past the block's n rows count as zero.  Every lane
+// of the wave calls both.
+template <int D>
+struct QueryRows {
+    static constexpr int CPR = D / 8;       // 16-byte chunks per row
+    static constexpr int RPI = 64 / CPR;    // rows per load instruction
+    static constexpr int ITER = 64 / RPI;   // load instructions per block
+    bf16x8 x[ITER];
+};
+
+template <int D>
+__device__ inline void query_rows_load(const bf16* qblk, int n, QueryRows<D>& qr) {
+    using R = QueryRows<D>;
+    const int lane = threadIdx.x & 63, c = lane % R::CPR, g = lane / R::CPR;
+    // (every load is issued -- rows past n re-read the last row and are
+    // zeroed afterwards -- so that no branch sits between the loads and the
+    // waits on them stay exact)
+#pragma unroll
+    for (int it = 0; it < R::ITER; ++it) {
+        const int r = g + R::RPI * it;
+        qr.x[it] = *reinterpret_cast<const bf16x8*>(qblk + (int64_t)(r < n ? r : n - 1) * D + 8 * c);
+    }
+#pragma unroll
+    for (int it = 0; it < R::ITER; ++it) {
+        if (g + R::RPI * it >= n) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qr.x[it][e] = (bf16)0.f;
+        }
+    }
+}
+
+template <int D>
+__device__ inline void query_rows_mean(const QueryRows<D>& qr, int n, float* qm) {
+    using R = QueryRows<D>;
+    const int lane = threadIdx.x & 63;
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < R::ITER; ++it)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += (float)qr.x[it][e];
+#pragma unroll
+    for (int m = R::CPR; m < 64; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += __shfl_xor(s[e], m, 64);
+    if (lane < R::CPR) {
+        const float fn = (float)n;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qm[8 * lane + e] = s[e] / fn;
+    }
+}
+
 // Routing in two parts, so that a caller can issue other memory loads
 // between them (route_scores waits for all of its own loads; route_select
 // issues none).  One wavefront (all 64 lanes of the workgroup).
 //
 // route_scores: srow[0..Nbp) = s_ij for every key block j (padding: 0).
-template <int D>
-__device__ inline void route_scores(const AttnArgs& a, int64_t bh, int64_t i, float* srow) {
+// The query mean comes from the pooled means in the workspace (fp32 inputs)
+// or, with FROM_Q (bf16), from the block's rows, formed in qm (D floats of
+// LDS) before the scores.
+template <int D, bool FROM_Q = false>
+__device__ inline void route_scores(const AttnArgs& a, int64_t bh, int64_t i, float* srow,
+                                    float* qm = nullptr) {
     const int lane = threadIdx.x & 63;
     const int64_t Nb = a.Nb, Nbp = a.Nbp;
     const float scale = 1.0f / sqrtf((float)D);
 
+    if constexpr (FROM_Q) {
+        const int n = (int)(a.N - i * 64 < 64 ? a.N - i * 64 : 64);
+        QueryRows<D> qr;
+        query_rows_load<D>(reinterpret_cast<const bf16*>(a.q) + (bh * a.N + i * 64) * D, n, qr);
+        query_rows_mean<D>(qr, n, qm);
+        __syncthreads();
+    }
+    const float* __restrict__ qb = FROM_Q ? qm : a.qbar + (bh * Nb + i) * D;
+
     // scores s_ij = qbar_i . kbar_j / sqrt(d); kbar is stored transposed so each
     // load instruction reads 1 KiB of consecutive key blocks.
-    const float* __restrict__ qb = a.qbar + (bh * Nb + i) * D;
     const float* __restrict__ kt = a.kbarT + bh * D * Nbp;
     // (rows of kbarT are loaded in batches of DB, DEPTH batches in flight:
     // the loads of batch b + DEPTH - 1 are issued before the FMAs of batch

@@ -2,7 +2,9 @@
 // attention kernels run as their prologue, launched on its own so that the
 // routing "setup" can be timed and exported (page "NVIDIA 與 SANA Sol-Engine"
 // news, section "技術組成": the pages report Sol-Attn's setup time on its own).
-// Routing reads only the fp32 pooled means, so one kernel serves both dtypes.
+// For fp32 inputs routing reads only the pooled means; for bf16 each query
+// block's mean is formed from its rows by the wave that routes it, as the
+// fused kernels' prologue forms it.
 #include "common.h"
 #include "launch.h"
 #include "route.h"
@@ -31,9 +33,22 @@ __global__ __launch_bounds__(64 * kRouteG) void route_kernel(AttnArgs a) {
     float* qs = smem + kRouteG * Nbp;
     uint16_t* klists = reinterpret_cast<uint16_t*>(qs + kRouteG * D);
     const int64_t klist_len = (Nb + 15) / 16 * 16;
-    for (int e = threadIdx.x; e < kRouteG * D; e += 64 * kRouteG) {
-        const int g = e / D, c = e % D;
-        qs[e] = i0 + g < Nb ? a.qbar[(bh * Nb + i0 + g) * D + c] : 0.f;
+    if (a.dtype == kBF16) {
+        // (wave-uniform branch: each wave forms its own block's mean)
+        if (i0 + wave < Nb) {
+            const int64_t i = i0 + wave;
+            const int n = (int)(a.N - i * 64 < 64 ? a.N - i * 64 : 64);
+            QueryRows<D> qr;
+            query_rows_load<D>(reinterpret_cast<const bf16*>(a.q) + (bh * a.N + i * 64) * D, n, qr);
+            query_rows_mean<D>(qr, n, qs + wave * D);
+        } else {
+            for (int c = lane; c < D; c += 64) qs[wave * D + c] = 0.f;
+        }
+    } else {
+        for (int e = threadIdx.x; e < kRouteG * D; e += 64 * kRouteG) {
+            const int g = e / D, c = e % D;
+            qs[e] = i0 + g < Nb ? a.qbar[(bh * Nb + i0 + g) * D + c] : 0.f;
+        }
     }
     __syncthreads();
     const float* __restrict__ kt = a.kbarT + bh * D * Nbp;

@@ -254,7 +254,7 @@ int scratch_ptr(void** out) {
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 PoolArgs pool_args(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t N,
-                   int64_t d, int mode, int dtype, void* ws, bool pack) {
+                   int64_t d, int mode, int dtype, void* ws, bool pack, bool export_qmeans = false) {
     const WsLayout L = ws_layout(B, H, N, d, dtype);
     PoolArgs p;
     p.q = q;
@@ -274,13 +274,15 @@ PoolArgs pool_args(const void* q, const void* k, const void* v, int64_t B, int64
     p.d = (int)d;
     p.dtype = dtype;
     p.pooled = (mode & SOLATTN_MODE_MASK) != SOLATTN_DENSE;
+    p.qmeans = dtype != kBF16 || export_qmeans;
     p.pack = pack && dtype == kBF16;
     return p;
 }
 
 int run_prepare(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t N,
-                int64_t d, int mode, int dtype, void* ws, hipStream_t s, bool pack) {
-    const PoolArgs p = pool_args(q, k, v, B, H, N, d, mode, dtype, ws, pack);
+                int64_t d, int mode, int dtype, void* ws, hipStream_t s, bool pack,
+                bool export_qmeans = false) {
+    const PoolArgs p = pool_args(q, k, v, B, H, N, d, mode, dtype, ws, pack, export_qmeans);
     if (!p.pooled && !p.pack) return SOLATTN_OK;  // fp32 dense: nothing to prepare
     hipError_t e = launch_pool(p, B * H, s);
     if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
@@ -550,7 +552,8 @@ int solattn_pool(const void* q, const void* k, const void* v, float* qbar, float
     const WsLayout L = ws_layout(B, H, N, d, dtype);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = internal_ws(L.total, s, &ws))) return rc;
-    if ((rc = run_prepare(q, k, v, B, H, N, d, SOLATTN_SPARSE, dtype, ws, s, false))) return rc;
+    if ((rc = run_prepare(q, k, v, B, H, N, d, SOLATTN_SPARSE, dtype, ws, s, false, true)))
+        return rc;
     const size_t bytes = sizeof(float) * B * H * ((N + 63) / 64) * d;
     const struct { float* dst; size_t off; } outs[3] = {{qbar, L.qbar}, {kbar, L.kbar}, {vbar, L.vbar}};
     for (const auto& o : outs) {
@@ -579,11 +582,13 @@ int solattn_route(const void* q, const void* k, const void* v, int64_t B, int64_
 int solattn_route_ws(const void* q, int64_t B, int64_t H, int64_t N, int64_t d,
                      int64_t prefix_len, float tau, int dtype, const void* ws, size_t ws_bytes,
                      uint32_t* mask_out, float* score_out, float* thr_out, void* stream) {
-    // reads only the pooled means in ws; q stands in for k and v in the checks
+    // reads the pooled key means in ws and the query means: for fp32 from ws,
+    // for bf16 formed from the query rows of q; q stands in for k and v in
+    // the checks
     int rc = validate(q, q, q, nullptr, false, B, H, N, d, prefix_len, tau, SOLATTN_SPARSE, dtype);
     if (rc) return rc;
     if ((rc = check_ws(const_cast<void*>(ws), ws_bytes, B, H, N, d, dtype))) return rc;
-    if ((rc = check_device_ptrs({ws, mask_out, score_out, thr_out}))) return rc;
+    if ((rc = check_device_ptrs({q, ws, mask_out, score_out, thr_out}))) return rc;
     return run_attend(q, q, q, nullptr, B, H, N, d, prefix_len, tau, SOLATTN_SPARSE, dtype,
                       const_cast<void*>(ws), static_cast<hipStream_t>(stream), mask_out, score_out,
                       thr_out, 1);

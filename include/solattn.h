@@ -220,9 +220,11 @@ int solattn_route(const void* q, const void* k, const void* v, int64_t B, int64_
  * same shape and dtype) has filled: the block scores, thresholds and keep
  * bits of every query block, with the exports of solattn_forward_debug (any
  * may be NULL).  The scoring pass on its own (page "Sol-H3" news, kocpc,
- * section "技術組成", reports the routing setup time on its own); reads only
- * the pooled means in ws, so q serves for the shape and alignment checks
- * only.  Allocates nothing.
+ * section "技術組成", reports the routing setup time on its own).  Reads the
+ * pooled key means in ws and the query means: for fp32 the ones prepare
+ * wrote to ws, for bf16 formed from the query rows of q (the bf16 kernels
+ * form each query block's mean from its rows; prepare writes none).
+ * Allocates nothing.
  */
 int solattn_route_ws(const void* q, int64_t B, int64_t H, int64_t N, int64_t d,
                      int64_t prefix_len, float tau, int dtype, const void* ws, size_t ws_bytes,
