@@ -1,7 +1,8 @@
 """Sol-Attn forward benchmark on one MI355X.
 
-A step is one full forward call (pooling kernel + fused routing/attention
-kernel) over the refine-stage workload: B=1, H=32, N = 256 text + 16128 video
+A step is one full forward call (pooling kernel, then the routing plan --
+routing kernel and dispatch-order kernel -- then the attention kernel, the
+launches solattn_forward_ws makes at this size) over the refine-stage workload: B=1, H=32, N = 256 text + 16128 video
 tokens (16x24x42 latent of a 1344x768, 121-frame clip), d=128, bf16, prefix
 256, tau=1.25, synthetic field inputs resident in HBM.  Prints one JSON line.
 
@@ -159,6 +160,23 @@ def cpu_baseline(q, k, v, w, tau, budget_s=15.0):
             "other_workloads": per}
 
 
+def stage_times(sa, stream, qd, out, prefix_len, tau, ws, n):
+    """Medians (ms) of the routing plan alone (solattn_plan_ws: the routing
+    and order kernels) and of the attention kernel alone
+    (solattn_attend_plan_ws), on a workspace prepared for the same inputs."""
+    import numpy as np
+
+    def plan():
+        sa.solattn_plan_ws(qd, prefix_len, tau, "sparse", ws)
+
+    def att():
+        sa.solattn_attend_plan_ws(qd, out, "sparse", ws)
+    plan()
+    pms = float(np.median(time_calls(plan, n, stream)))
+    ams = float(np.median(time_calls(att, n, stream)))
+    return pms, ams
+
+
 def draft_check(sa, stream):
     """The draft-stage shape at the tau whose video block sparsity is ~90 %
     (tests/golden/draft_tau.json, calibrated with the oracle's routing):
@@ -203,7 +221,8 @@ def draft_check(sa, stream):
         sparse()
     sms = float(np.median(time_calls(sparse, 20, stream)))
     prep()
-    ams = float(np.median(time_calls(attend, 20, stream)))
+    cms = float(np.median(time_calls(attend, 20, stream)))
+    plan_ms, ams = stage_times(sa, stream, qd, out, w.prefix_len, tau, ws, 20)
     for _ in range(3):
         topk()
     tms = float(np.median(time_calls(topk, 20, stream)))
@@ -212,7 +231,8 @@ def draft_check(sa, stream):
     kept_tflops = fk / (ams * 1e-3) / 1e12
     return {"workload": "draft: 672x384 -> 32x24x42 latent, 512 prefix + 32256 video tokens",
             "N": w.N, "tau": tau, "video_sparsity": round(float(1 - m[..., pb:].mean()), 4),
-            "sparse_ms": round(sms, 4), "attn_ms": round(ams, 4), "dense_ms": round(dms, 3),
+            "sparse_ms": round(sms, 4), "attend_call_ms": round(cms, 4),
+            "plan_ms": round(plan_ms, 4), "attn_ms": round(ams, 4), "dense_ms": round(dms, 3),
             "speedup_vs_dense": round(dms / sms, 2),
             "dense_equiv_tflops": round(4.0 * w.B * w.H * w.N * w.N * w.D / (sms * 1e-3) / 1e12, 1),
             "kept_tile_tflop": round(fk / 1e12, 4), "pooled_tflop": round(fp / 1e12, 5),
@@ -353,7 +373,8 @@ def long_clip_check(sa, stream):
     cms = float(np.median(time_calls(call, 10, stream)))
     pms = float(np.median(time_calls(prep, 10, stream)))
     prep()
-    ams = float(np.median(time_calls(attend, 10, stream)))
+    acms = float(np.median(time_calls(attend, 10, stream)))
+    plan_ms, ams = stage_times(sa, stream, qd, out, w.prefix_len, tau, ws, 10)
     mw = torch.zeros((w.B, w.H, w.nb, (w.nb + 31) // 32), dtype=torch.int32, device="cuda")
     th = torch.zeros((w.B, w.H, w.nb), dtype=torch.float32, device="cuda")
 
@@ -373,6 +394,8 @@ def long_clip_check(sa, stream):
             "pool_GBps": round(pool_bytes(w.B, w.H, w.N, w.D) / (pms * 1e-3) / 1e9, 1),
             "setup_ms": round(sms, 4),
             "scoring_pass": score,
+            "attend_call_ms": round(acms, 4),
+            "plan_ms": round(plan_ms, 4),
             "attn_ms": round(ams, 4),
             "kept_tile_tflop": round(fk / 1e12, 4), "pooled_tflop": round(fp / 1e12, 5),
             "attn_kept_tflops": round(tflops, 1),
@@ -663,29 +686,36 @@ def main():
     log("tau %.3g: kept blocks/row %.1f of %d, video skip %.4f" % (tau, mask.sum(-1).mean(), w.nb,
                                                                    video_skip))
 
+    # one call = pooling, the routing plan (routing kernel + order kernel)
+    # and the attention kernel: the launches solattn_forward_ws makes at this
+    # size, issued through the stage entry points so that each is timed
     def step():
         sa.solattn_prepare_ws(qd, kd, vd, "sparse", ws)
-        sa.solattn_attend_ws(qd, kd, vd, out, w.prefix_len, tau, "sparse", ws)
+        sa.solattn_plan_ws(qd, w.prefix_len, tau, "sparse", ws)
+        sa.solattn_attend_plan_ws(qd, out, "sparse", ws)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-kernel HIP events on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # timed region: K steps, per-stage HIP events on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
         sa.solattn_prepare_ws(qd, kd, vd, "sparse", ws)
         ev[i][1].record(stream)
-        sa.solattn_attend_ws(qd, kd, vd, out, w.prefix_len, tau, "sparse", ws)
+        sa.solattn_plan_ws(qd, w.prefix_len, tau, "sparse", ws)
         ev[i][2].record(stream)
+        sa.solattn_attend_plan_ws(qd, out, "sparse", ws)
+        ev[i][3].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1000.0 / args.steps
     pool_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    call_list = [e[0].elapsed_time(e[2]) for e in ev]
+    plan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    call_list = [e[0].elapsed_time(e[3]) for e in ev]
     call_ms = float(np.mean(call_list))
     ms_per_step = wall_ms  # wall clock over the K steps, synchronised on both sides
 
@@ -715,6 +745,7 @@ def main():
         "gpu_event_ms_per_call": round(call_ms, 4),
         "call_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(call_list, [10, 50, 90])],
         "pool_ms": round(pool_ms, 4),
+        "plan_ms": round(plan_ms, 4),
         "attn_ms": round(attn_ms, 4),
         "pool_read_GBps": round(pool_read / (pool_ms * 1e-3) / 1e9, 1),
         "pool_GBps": round(pool_bytes(B, H, N, d) / (pool_ms * 1e-3) / 1e9, 1),

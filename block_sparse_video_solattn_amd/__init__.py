@@ -8,7 +8,8 @@ generators in ``.inputs`` need no library.
 _BINDING_NAMES = (
     "BF16", "DENSE", "EXPORTS", "F32", "PREFIX_ROWS", "SPARSE", "TAYLOR1", "TOPK", "VIDEO_STATS",
     "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "ENOMEM", "NOALLOC_SCRATCH_BYTES",
-    "SolAttnError", "solattn_attend_ws", "solattn_forward_noalloc",
+    "SolAttnError", "solattn_attend_ws", "solattn_forward_noalloc", "solattn_plan_ws",
+    "solattn_attend_plan_ws",
     "solattn_forward", "solattn_forward_debug", "solattn_forward_ws", "solattn_last_error",
     "solattn_pool", "solattn_prepare_ws", "solattn_probe_mfma_bf16", "solattn_route", "solattn_route_ws",
     "solattn_strerror",

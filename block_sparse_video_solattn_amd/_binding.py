@@ -49,6 +49,8 @@ _SIGS = {
     "solattn_forward_ws": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P, _SZ, _P], _I),
     "solattn_prepare_ws": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I, _I, _P, _SZ, _P], _I),
     "solattn_attend_ws": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P, _SZ, _P], _I),
+    "solattn_plan_ws": ([_P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P, _SZ, _P], _I),
+    "solattn_attend_plan_ws": ([_P, _P, _I64, _I64, _I64, _I64, _I, _I, _P, _SZ, _P], _I),
     "solattn_forward_debug": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P, _P, _P, _P], _I),
     "solattn_pool": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P], _I),
     "solattn_route": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I, _P, _P, _P, _P], _I),
@@ -236,6 +238,24 @@ def solattn_attend_ws(q, k, v, out, prefix_len, tau, mode, ws, stream=None):
     _check(_lib.solattn_attend_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, prefix_len,
                                   float(tau), _mode_code(mode), _dtype_code(q), _ptr(ws),
                                   _ws_bytes(q, ws), _stream(stream)))
+    return out
+
+
+def solattn_plan_ws(q, prefix_len, tau, mode, ws, stream=None):
+    """Routing plan (keep bits, tile counts, dispatch order) into ws, which
+    solattn_prepare_ws filled for q's shape (bf16 sparse / topk)."""
+    B, H, N, d = _shape(q)
+    _check(_lib.solattn_plan_ws(_ptr(q), B, H, N, d, prefix_len, float(tau), _mode_code(mode),
+                                _dtype_code(q), _ptr(ws), _ws_bytes(q, ws), _stream(stream)))
+
+
+def solattn_attend_plan_ws(q, out, mode, ws, stream=None):
+    """Attention in the order and with the routing solattn_plan_ws left in ws."""
+    B, H, N, d = _shape(q)
+    _check_like(q, out)
+    _check(_lib.solattn_attend_plan_ws(_ptr(q), _ptr(out), B, H, N, d, _mode_code(mode),
+                                       _dtype_code(q), _ptr(ws), _ws_bytes(q, ws),
+                                       _stream(stream)))
     return out
 
 

@@ -650,17 +650,26 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
 
     const int lane = threadIdx.x, half = lane >> 5, l32 = lane & 31;
     const int64_t N = a.N, Nb = a.Nb, Nbp = a.Nbp;
-    const int64_t w = work_order(blockIdx.x, a.BH * Nb, Nb, a.Pb,
-                                 a.mode != kDense && a.prefix_rows);
+    // A planned launch (the routing kernel and the order kernel ran first)
+    // takes its work item from the dispatch order and its routing from the
+    // keep bits; otherwise the work item follows work_order and the wave
+    // routes its query block itself.
+    const bool planned = a.plan_perm != nullptr;
+    const int64_t w = planned ? (int64_t)__builtin_amdgcn_readfirstlane(
+                                    a.plan_perm[xcd_remap(blockIdx.x, a.BH * Nb)])
+                              : work_order(blockIdx.x, a.BH * Nb, Nb, a.Pb,
+                                           a.mode != kDense && a.prefix_rows);
     const int64_t bh = w / Nb, i = w % Nb;
     // LDS: srow[Nbp] routing scores, then pooled-key biases; two 64-entry
     // bias rows for exact tiles (all zero; zero then -inf past the tail
     // block's last key; before that, the block's query mean while the
-    // scores are formed); the kept list; the pooled-tile list
+    // scores are formed); the kept list; the pooled-tile list; a planned
+    // launch's keep bits (Nbp / 32 words)
     float* srow = smem;
     const int zero_bias = (int)Nbp, tail_bias = (int)Nbp + 64;
     uint16_t* klist = reinterpret_cast<uint16_t*>(smem + Nbp + 128);
     uint16_t* plist = reinterpret_cast<uint16_t*>(smem + Nbp + 128 + (Nb + 15) / 16 * 8);
+    uint32_t* kbits = reinterpret_cast<uint32_t*>(smem + Nbp + 128 + (Nb + 15) / 16 * 8 + 32);
 
     const bf16* qp = reinterpret_cast<const bf16*>(a.q) + bh * N * D;
     const bf16* kp = reinterpret_cast<const bf16*>(a.kP) + bh * Nb * D * 64;
@@ -673,7 +682,16 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     // query block: lane holds query 32*nt + l32, d = 16*s + 8*half .. +7.
     // Loaded between the two parts of the routing, so that the block's trip
     // from HBM overlaps the threshold and keep-mask work.
-    if (a.mode != kDense) route_scores<D, true>(a, bh, i, srow, srow + Nbp);
+    // (planned: the row's keep bits are requested ahead of the Q loads, lane
+    // l taking word l; rows of more than 64 words take the rest after them)
+    const int64_t W = (Nb + 31) / 32;
+    const uint32_t* brow = planned ? a.plan_mask + (bh * Nb + i) * W : nullptr;
+    uint32_t bits0 = 0;
+    if (planned) {
+        if (lane < W) bits0 = brow[lane];
+    } else if (a.mode != kDense) {
+        route_scores<D, true>(a, bh, i, srow, srow + Nbp);
+    }
     bf16x8 qB[2][KS];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -685,7 +703,14 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(AttnArgs a) {
     }
     int n_kept;
     uint64_t tile_mask;
-    if (a.mode != kDense) {
+    if (planned) {
+        if (lane < W) kbits[lane] = bits0;
+        for (int64_t k = 64 + lane; k < W; k += 64) kbits[k] = brow[k];
+        __syncthreads();
+        const RouteResult r = route_from_bits(a, bh, i, kbits, srow, klist);
+        n_kept = r.n_kept;
+        tile_mask = r.tile_mask;
+    } else if (a.mode != kDense) {
         const RouteResult r = route_select(a, bh, i, srow, klist);
         n_kept = r.n_kept;
         tile_mask = r.tile_mask;
@@ -897,7 +922,7 @@ hipError_t launch_attn_bf16_taylor(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-    const size_t lds = sizeof(float) * (a.Nbp + 128 + (a.Nb + 15) / 16 * 8 + 32);
+    const size_t lds = sizeof(float) * (a.Nbp + 128 + (a.Nb + 15) / 16 * 8 + 32 + a.Nbp / 32);
     const dim3 grid((unsigned)(a.BH * a.Nb));
     if (a.d == 128)
         hipLaunchKernelGGL((attn_bf16_kernel<128>), grid, dim3(64), lds, s, a);

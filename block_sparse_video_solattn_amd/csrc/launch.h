@@ -21,8 +21,13 @@ enum Mode { kDense = 0, kSparse = 1, kTopk = 2 };
 //   vbarP             bf16 [BH][Nbp/64][d*64] pooled values, MFMA operand order
 //   kP                bf16 [BH][Nb][64*d]  key tiles, MFMA operand order
 //   vP                bf16 [BH][Nb][d*64]  value tiles, MFMA operand order
+//   plan_mask         u32  [BH][Nb][ceil(Nb/32)] routed keep bits (bf16 only;
+//                                          bit j%32 of word j/32 in row i)
+//   plan_cost         i32  [BH*Nb]         tiles each query block will run
+//   plan_perm         i32  [BH*Nb]         dispatch order: work item of each
+//                                          launch position
 struct WsLayout {
-    size_t qbar, kbar, vbar, kbarT, kbarP, vbarP, kP, vP, total;
+    size_t qbar, kbar, vbar, kbarT, kbarP, vbarP, kP, vP, plan_mask, plan_cost, plan_perm, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -41,8 +46,11 @@ inline WsLayout ws_layout(int64_t B, int64_t H, int64_t N, int64_t d, int dtype)
         w.vbarP = take(2 * BH * Nbp * d);
         w.kP = take(2 * BH * Nb * 64 * d);
         w.vP = take(2 * BH * Nb * 64 * d);
+        w.plan_mask = take(sizeof(uint32_t) * BH * Nb * ((Nb + 31) / 32));
+        w.plan_cost = take(sizeof(int32_t) * BH * Nb);
+        w.plan_perm = take(sizeof(int32_t) * BH * Nb);
     } else {
-        w.kbarP = w.vbarP = w.kP = w.vP = 0;
+        w.kbarP = w.vbarP = w.kP = w.vP = w.plan_mask = w.plan_cost = w.plan_perm = 0;
     }
     w.total = off;
     return w;
@@ -92,6 +100,14 @@ struct AttnArgs {
     int d, dtype, mode;   // mode: kDense, kSparse or kTopk (the flags below apart)
     int prefix_rows;      // query blocks i < Pb keep every key block
     int video_stats;      // kSparse: threshold statistics over key blocks j >= Pb
+    // Routing plan (bf16 kSparse / kTopk).  The routing kernel writes the keep
+    // bits and tile counts when plan_mask / plan_cost are set; the order
+    // kernel writes plan_perm from plan_cost; the attention kernel, given
+    // plan_perm, takes its work item from it and its routing from plan_mask
+    // instead of routing the query block itself.  NULL: no plan.
+    uint32_t* plan_mask;
+    int32_t* plan_cost;
+    int32_t* plan_perm;
 };
 
 // Sequence-parallel transport (transport.hip); record = d codes + fp32 scale,
@@ -139,6 +155,7 @@ hipError_t launch_unpack_pool(const PoolArgs& a, const UnpackPoolArgs& u, hipStr
 
 hipError_t launch_pool(const PoolArgs& a, int64_t BH, hipStream_t s);
 hipError_t launch_route(const AttnArgs& a, hipStream_t s);
+hipError_t launch_order(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 

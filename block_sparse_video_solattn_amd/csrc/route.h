@@ -20,9 +20,12 @@
 // In the fixed-ratio mode the threshold is instead the k-th largest video
 // score of the row (kth_largest_video) and skipped blocks get no pooled term.
 //
-// Nothing of the routing reaches device memory except through the debug
-// exports: the mask lives as ballot words, the kept-block list and the
-// pooled-term biases in LDS.
+// In a fused launch nothing of the routing reaches device memory except
+// through the debug exports: the mask lives as ballot words, the kept-block
+// list and the pooled-term biases in LDS.  A planning launch (the routing
+// kernel, ahead of a planned attention launch) also writes each row's keep
+// bits and tile count to the workspace, and the planned attention kernel
+// rebuilds the same lists and biases from those bits.
 #pragma once
 
 #include "common.h"
@@ -204,14 +207,60 @@ __device__ inline void route_scores(const AttnArgs& a, int64_t bh, int64_t i, fl
     __syncthreads();
 }
 
-// route_select, from the scores in srow (one wavefront).  On return:
+// The lists of a routed query block from its keep decisions: keep(j, s_j)
+// for every key block j < Nb (s_j = srow[j]; a planned launch passes keep
+// bits instead and its srow holds no scores yet).  On return:
 //   klist[0..n_kept)  kept key-block indices (ascending)
 //   srow[0..Nbp)      log2(n_j) for skipped blocks, -inf for kept and padding
 //                     (the per-column bias of the pooled tiles, log2 units)
+// and the keep bits, with the scores for score_out, are written to any of
+// the given destinations ([BH][Nb][ceil(Nb/32)] words, [BH][Nb][Nb] floats).
+template <class Keep>
+__device__ inline RouteResult route_lists(const AttnArgs& a, int64_t bh, int64_t i, float* srow,
+                                          uint16_t* klist, Keep keep, float* score_out,
+                                          uint32_t* mask_out, uint32_t* plan_out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t Nb = a.Nb, Nbp = a.Nbp;
+    // keep bits, kept list, pooled-tile flags, pooled biases (log2 n_j: 6
+    // for a full block, log2 of its key count for a ragged last block)
+    int n_kept = 0;
+    uint64_t tile_mask = 0;
+    const int64_t W = (Nb + 31) / 32;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int nb = (int)Nb, nbp = (int)Nbp;
+    const float log2_last = log2f((float)(a.N - (Nb - 1) * 64));
+    for (int j0 = 0; j0 < nbp; j0 += 64) {
+        const int j = j0 + lane;
+        const bool valid = j < nb;
+        const float s = srow[j];
+        const bool kp = valid && keep(j, s);
+        const bool skip = valid && !kp;
+        const uint64_t kb = __ballot(kp);
+        const uint64_t sb = __ballot(skip);
+        if (score_out && valid) score_out[(bh * Nb + i) * Nb + j] = s;
+        const int64_t w0 = j0 / 32;
+        for (uint32_t* dst : {mask_out, plan_out}) {
+            if (!dst) continue;
+            if (lane == 0 && w0 < W) dst[(bh * Nb + i) * W + w0] = (uint32_t)kb;
+            if (lane == 1 && w0 + 1 < W) dst[(bh * Nb + i) * W + w0 + 1] = (uint32_t)(kb >> 32);
+        }
+        if (kp) klist[n_kept + __popcll(kb & lt)] = (uint16_t)j;
+        n_kept += __popcll(kb);
+        if (sb && a.mode == kSparse) tile_mask |= 1ull << (j0 / 64);  // pooled terms: Sol-Attn only
+        srow[j] = skip ? (j == nb - 1 ? log2_last : 6.0f) : -__builtin_inff();
+    }
+    // (no workgroup barrier here: the lists are this wave's own LDS; callers
+    // synchronise before other waves, or later code, read them)
+    return RouteResult{n_kept, tile_mask};
+}
+
+// route_select, from the scores in srow (one wavefront): the threshold, then
+// route_lists with keep_j = (j < Pb or s_j >= threshold), writing the debug
+// exports and, in a planning launch, the keep bits to plan_mask.
 __device__ inline RouteResult route_select(const AttnArgs& a, int64_t bh, int64_t i, float* srow,
                                            uint16_t* klist) {
     const int lane = threadIdx.x & 63;
-    const int64_t Nb = a.Nb, Nbp = a.Nbp;
+    const int64_t Nb = a.Nb;
     float thr;
     if (a.prefix_rows && i < a.Pb) {
         thr = -__builtin_inff();  // a prefix query block keeps every key block
@@ -239,38 +288,23 @@ __device__ inline RouteResult route_select(const AttnArgs& a, int64_t bh, int64_
             thr = sigma == 0.f ? mu : mu + a.tau * sigma;
         }
     }
-
-    // keep bits, kept list, pooled-tile flags, pooled biases (log2 n_j: 6
-    // for a full block, log2 of its key count for a ragged last block)
-    int n_kept = 0;
-    uint64_t tile_mask = 0;
-    const int64_t W = (Nb + 31) / 32;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int nb = (int)Nb, nbp = (int)Nbp, pb = (int)a.Pb;
-    const float log2_last = log2f((float)(a.N - (Nb - 1) * 64));
-    for (int j0 = 0; j0 < nbp; j0 += 64) {
-        const int j = j0 + lane;
-        const bool valid = j < nb;
-        const float s = srow[j];
-        const bool keep = valid && (j < pb || s >= thr);
-        const bool skip = valid && !keep;
-        const uint64_t kb = __ballot(keep);
-        const uint64_t sb = __ballot(skip);
-        if (a.score_out && valid) a.score_out[(bh * Nb + i) * Nb + j] = s;
-        if (a.mask_out) {
-            const int64_t w0 = j0 / 32;
-            if (lane == 0 && w0 < W) a.mask_out[(bh * Nb + i) * W + w0] = (uint32_t)kb;
-            if (lane == 1 && w0 + 1 < W) a.mask_out[(bh * Nb + i) * W + w0 + 1] = (uint32_t)(kb >> 32);
-        }
-        if (keep) klist[n_kept + __popcll(kb & lt)] = (uint16_t)j;
-        n_kept += __popcll(kb);
-        if (sb && a.mode == kSparse) tile_mask |= 1ull << (j0 / 64);  // pooled terms: Sol-Attn only
-        srow[j] = skip ? (j == nb - 1 ? log2_last : 6.0f) : -__builtin_inff();
-    }
+    const int pb = (int)a.Pb;
+    const RouteResult r = route_lists(
+        a, bh, i, srow, klist, [&](int j, float s) { return j < pb || s >= thr; }, a.score_out,
+        a.mask_out, a.plan_mask);
     if (a.thr_out && lane == 0) a.thr_out[bh * Nb + i] = thr;
-    // (no workgroup barrier here: the lists are this wave's own LDS; callers
-    // synchronise before other waves, or later code, read them)
-    return RouteResult{n_kept, tile_mask};
+    return r;
+}
+
+// The routing of query block i from its keep bits (a planned launch): the
+// row's ceil(Nb/32) words, already in LDS at words[], through route_lists;
+// the same lists and biases route_select leaves for the same bits.
+__device__ inline RouteResult route_from_bits(const AttnArgs& a, int64_t bh, int64_t i,
+                                              const uint32_t* words, float* srow,
+                                              uint16_t* klist) {
+    return route_lists(
+        a, bh, i, srow, klist, [&](int j, float) { return (words[j >> 5] >> (j & 31)) & 1u; },
+        nullptr, nullptr, nullptr);
 }
 
 template <int D>

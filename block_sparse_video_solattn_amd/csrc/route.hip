@@ -1,7 +1,10 @@
-// Routing alone (steps 1-2 without attention): the same device code the fused
-// attention kernels run as their prologue, launched on its own so that the
-// routing "setup" can be timed and exported (page "NVIDIA 與 SANA Sol-Engine"
-// news, section "技術組成": the pages report Sol-Attn's setup time on its own).
+// Routing alone (steps 1-2 without attention; page "NVIDIA 與 SANA
+// Sol-Engine" news, section "技術組成", reports Sol-Attn's setup time on its
+// own): the same device code the fused attention kernels run as their
+// prologue, launched on its own so that the routing can be timed and
+// exported -- and ahead of a planned attention launch, for which it also
+// writes each query block's keep bits and tile count to the workspace (the
+// order kernel below then fixes the dispatch order from the counts).
 // For fp32 inputs routing reads only the pooled means; for bf16 each query
 // block's mean is formed from its rows by the wave that routes it, as the
 // fused kernels' prologue forms it.
@@ -67,8 +70,66 @@ __global__ __launch_bounds__(64 * kRouteG) void route_kernel(AttnArgs a) {
         for (int g = 0; g < kRouteG; ++g) smem[g * Nbp + j] = acc[g] * scale;
     }
     __syncthreads();
-    if (i0 + wave < Nb)
-        (void)route_select(a, bh, i0 + wave, smem + wave * Nbp, klists + wave * klist_len);
+    if (i0 + wave < Nb) {
+        const RouteResult r =
+            route_select(a, bh, i0 + wave, smem + wave * Nbp, klists + wave * klist_len);
+        // tiles the attention kernel will run for this block: kept blocks
+        // plus pooled tiles (the dispatch order's cost estimate)
+        if (a.plan_cost && lane == 0)
+            a.plan_cost[bh * Nb + i0 + wave] = r.n_kept + __popcll(r.tile_mask);
+    }
+}
+
+// Dispatch order of a planned attention launch.  The launch gives XCD x the
+// contiguous range of launch positions xcd_remap assigns it; position p runs
+// work item plan_perm[p].  Within the part of one head that falls in one
+// XCD's range, items are placed in decreasing tile count (ties: ascending
+// index), longest-processing-time-first list scheduling: the XCD's compute
+// units take positions in order as they free up, so its last dispatch round
+// holds its shortest items instead of whichever items the sequence put last.
+// Items of one head stay together, so the head's key/value tiles stay shared
+// in that XCD's L2.  One workgroup ranks 256 items of one head against the
+// head's counts in LDS.
+__global__ __launch_bounds__(256) void order_kernel(AttnArgs a) {
+    extern __shared__ int32_t cnt[];
+    // (B*H*Nb < 2^31 is checked on the host: 32-bit indices)
+    const int Nb = (int)a.Nb, T = (int)(a.BH * a.Nb);
+    const int chunks = (Nb + 255) / 256;
+    const int bh = (int)blockIdx.x / chunks, h0 = bh * Nb;
+    for (int e = threadIdx.x; e < Nb; e += 256) cnt[e] = a.plan_cost[h0 + e];
+    __syncthreads();
+    const int e = ((int)blockIdx.x % chunks) * 256 + (int)threadIdx.x;
+    if (e >= Nb) return;
+    // the XCD range holding position h0 + e (xcd_remap: 8 ranges, the first
+    // T % 8 of them one position longer), clipped to this head
+    const int g = h0 + e, q = T / 8, m = T % 8;
+    const int x = g < m * (q + 1) ? g / (q + 1) : m + (g - m * (q + 1)) / (q > 0 ? q : 1);
+    const int x_lo = x * q + (x < m ? x : m), x_hi = x_lo + q + (x < m ? 1 : 0);
+    const int lo = (x_lo > h0 ? x_lo : h0) - h0;
+    const int hi = (x_hi < h0 + Nb ? x_hi : h0 + Nb) - h0;
+    const int32_t c = cnt[e];
+    int rank = 0;
+    // (every lane reads the same count at once: LDS broadcasts; unrolled so
+    // that several reads are in flight)
+#pragma unroll 8
+    for (int f = lo; f < hi; ++f) {
+        const int32_t cf = cnt[f];
+        rank += (cf > c) | ((cf == c) & (f < e));
+    }
+    a.plan_perm[h0 + lo + rank] = g;
+}
+
+hipError_t launch_order(const AttnArgs& a, hipStream_t s) {
+    const size_t lds = sizeof(int32_t) * a.Nb;
+    const dim3 grid((unsigned)(a.BH * ((a.Nb + 255) / 256)));
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&order_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(order_kernel, grid, dim3(256), lds, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_route(const AttnArgs& a, hipStream_t s) {

@@ -289,10 +289,30 @@ int run_prepare(const void* q, const void* k, const void* v, int64_t B, int64_t 
     return SOLATTN_OK;
 }
 
+// Steps of run_attend: all of steps 2-5 (kStageAll), the routing alone with
+// its exports (kStageRouteOnly), the routing plan alone (kStagePlan: keep
+// bits, tile counts and the dispatch order into the workspace) and the
+// attention from a plan already in the workspace (kStageAttendPlan).
+enum Stage { kStageAll = 0, kStageRouteOnly = 1, kStagePlan = 2, kStageAttendPlan = 3 };
+
+// Launches of B*H*Nb work items from this many on take the planned route in
+// kStageAll: routing kernel, order kernel, then attention in the planned
+// order.  Below it the launch is at most ~2 dispatch rounds of the chip's
+// 1024 wave slots, where the order cannot shorten the last round and the
+// two extra launches cost more than the routing they take out of the
+// attention kernel.
+constexpr int64_t kPlanMinItems = 2048;
+
+bool plannable(int mode, int dtype) {
+    const int base = mode & SOLATTN_MODE_MASK;
+    return dtype == SOLATTN_BF16 && base != SOLATTN_DENSE && !(mode & SOLATTN_TAYLOR1);
+}
+
 int run_attend(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
                int64_t N, int64_t d, int64_t prefix_len, float tau, int mode, int dtype, void* ws,
                hipStream_t s, uint32_t* mask_out, float* score_out, float* thr_out,
-               int route_only) {
+               int stage) {
+    const int route_only = stage == kStageRouteOnly;
     const WsLayout L = ws_layout(B, H, N, d, dtype);
     AttnArgs a;
     a.q = q;
@@ -328,6 +348,38 @@ int run_attend(const void* q, const void* k, const void* v, void* out, int64_t B
         const int64_t nv = a.Nb - a.Pb;
         int64_t kk = base == SOLATTN_TOPK ? (int64_t)std::ceil((double)tau * (double)nv) : 0;
         a.topk = kk > nv ? nv : kk;
+    }
+    a.plan_mask = nullptr;
+    a.plan_cost = nullptr;
+    a.plan_perm = nullptr;
+    const bool plan = stage == kStagePlan || stage == kStageAttendPlan ||
+                      (stage == kStageAll && plannable(mode, dtype) && a.BH * a.Nb >= kPlanMinItems);
+    if (plan) {
+        uint32_t* pm = reinterpret_cast<uint32_t*>(at(ws, L.plan_mask));
+        int32_t* pc = reinterpret_cast<int32_t*>(at(ws, L.plan_cost));
+        int32_t* pp = reinterpret_cast<int32_t*>(at(ws, L.plan_perm));
+        if (stage != kStageAttendPlan) {
+            // routing with the debug exports, keep bits and tile counts; then
+            // the dispatch order from the counts
+            a.plan_mask = pm;
+            a.plan_cost = pc;
+            hipError_t e = launch_route(a, s);
+            if (e != hipSuccess) return hip_fail(e, "route kernel launch");
+            a.plan_perm = pp;
+            e = launch_order(a, s);
+            if (e != hipSuccess) return hip_fail(e, "order kernel launch");
+            if (stage == kStagePlan) return SOLATTN_OK;
+        }
+        // attention in the planned order, its routing from the keep bits
+        a.plan_mask = pm;
+        a.plan_cost = nullptr;
+        a.plan_perm = pp;
+        a.mask_out = nullptr;
+        a.score_out = nullptr;
+        a.thr_out = nullptr;
+        const hipError_t e = launch_attn_bf16(a, s);
+        if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+        return SOLATTN_OK;
     }
     hipError_t e = route_only                  ? launch_route(a, s)
                    : (mode & SOLATTN_TAYLOR1) ? launch_attn_bf16_taylor(a, s)
@@ -525,6 +577,40 @@ int solattn_attend_ws(const void* q, const void* k, const void* v, void* out, in
                       static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, 0);
 }
 
+int solattn_plan_ws(const void* q, int64_t B, int64_t H, int64_t N, int64_t d,
+                    int64_t prefix_len, float tau, int mode, int dtype, void* ws, size_t ws_bytes,
+                    void* stream) {
+    // q stands in for k and v in the checks (the routing reads q and ws)
+    int rc = validate(q, q, q, nullptr, false, B, H, N, d, prefix_len, tau, mode, dtype);
+    if (rc) return rc;
+    if ((mode & SOLATTN_MODE_MASK) == SOLATTN_TOPK && !(tau > 0.f && tau <= 1.f))
+        return fail(SOLATTN_EINVAL, "topk mode: tau is the kept fraction, in (0, 1] (got %g)",
+                    (double)tau);
+    if (!plannable(mode, dtype))
+        return fail(SOLATTN_EUNSUPPORTED, "a routing plan is built for bf16 SPARSE or TOPK "
+                                          "without SOLATTN_TAYLOR1 only");
+    if ((rc = check_ws(ws, ws_bytes, B, H, N, d, dtype))) return rc;
+    if ((rc = check_device_ptrs({q, ws}))) return rc;
+    return run_attend(q, q, q, nullptr, B, H, N, d, prefix_len, tau, mode, dtype, ws,
+                      static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, kStagePlan);
+}
+
+int solattn_attend_plan_ws(const void* q, void* out, int64_t B, int64_t H, int64_t N, int64_t d,
+                           int mode, int dtype, void* ws, size_t ws_bytes, void* stream) {
+    // keys and values come from the workspace tiles; the routing from the
+    // plan (prefix length and tau are in the keep bits already)
+    int rc = validate(q, q, q, out, true, B, H, N, d, 0, 1.f, mode, dtype);
+    if (rc) return rc;
+    if (!plannable(mode, dtype))
+        return fail(SOLATTN_EUNSUPPORTED, "a routing plan is built for bf16 SPARSE or TOPK "
+                                          "without SOLATTN_TAYLOR1 only");
+    if ((rc = check_ws(ws, ws_bytes, B, H, N, d, dtype))) return rc;
+    if ((rc = check_device_ptrs({q, out, ws}))) return rc;
+    return run_attend(q, nullptr, nullptr, out, B, H, N, d, 0, 1.f, mode, dtype, ws,
+                      static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr,
+                      kStageAttendPlan);
+}
+
 int solattn_forward_debug(const void* q, const void* k, const void* v, void* out, int64_t B,
                           int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau,
                           int mode, int dtype, uint32_t* mask_out, float* score_out,
@@ -576,7 +662,7 @@ int solattn_route(const void* q, const void* k, const void* v, int64_t B, int64_
     if ((rc = internal_ws(ws_layout(B, H, N, d, dtype).total, s, &ws))) return rc;
     if ((rc = run_prepare(q, k, v, B, H, N, d, SOLATTN_SPARSE, dtype, ws, s, false))) return rc;
     return run_attend(q, k, v, nullptr, B, H, N, d, prefix_len, tau, SOLATTN_SPARSE, dtype, ws, s,
-                      mask_out, score_out, thr_out, 1);
+                      mask_out, score_out, thr_out, kStageRouteOnly);
 }
 
 int solattn_route_ws(const void* q, int64_t B, int64_t H, int64_t N, int64_t d,
@@ -591,7 +677,7 @@ int solattn_route_ws(const void* q, int64_t B, int64_t H, int64_t N, int64_t d,
     if ((rc = check_device_ptrs({q, ws, mask_out, score_out, thr_out}))) return rc;
     return run_attend(q, q, q, nullptr, B, H, N, d, prefix_len, tau, SOLATTN_SPARSE, dtype,
                       const_cast<void*>(ws), static_cast<hipStream_t>(stream), mask_out, score_out,
-                      thr_out, 1);
+                      thr_out, kStageRouteOnly);
 }
 
 const char* solattn_strerror(int code) {

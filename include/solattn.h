@@ -124,8 +124,11 @@ extern "C" {
 #define SOLATTN_BF16 1
 
 /*
- * Full forward pass: pooling (step 1) then the fused routing + attention
- * kernel (steps 2-5).  In DENSE mode tau and prefix_len are ignored and no
+ * Full forward pass: pooling (step 1) then steps 2-5 -- for launches of
+ * B*H*ceil(N/64) >= 2048 query blocks in bf16 SPARSE / TOPK the routing
+ * plan and the attention that follows it (solattn_plan_ws and
+ * solattn_attend_plan_ws below), otherwise one kernel that routes each
+ * query block and attends.  In DENSE mode tau and prefix_len are ignored and no
  * pooling is done; in TOPK mode tau is the kept fraction (outside (0, 1]:
  * SOLATTN_EINVAL).  Uses the internal workspace of (current device,
  * stream), allocated or grown on first need.
@@ -184,6 +187,35 @@ int solattn_prepare_ws(const void* q, const void* k, const void* v, int64_t B, i
 int solattn_attend_ws(const void* q, const void* k, const void* v, void* out, int64_t B,
                       int64_t H, int64_t N, int64_t d, int64_t prefix_len, float tau, int mode,
                       int dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * solattn_attend_ws split in two for bf16 SPARSE and TOPK (with either
+ * routing flag; not SOLATTN_TAYLOR1): the routing plan, then the attention
+ * that follows it.  For launches of B*H*ceil(N/64) >= 2048 query blocks
+ * solattn_attend_ws runs exactly these two steps; below that it routes
+ * inside the attention kernel.  The output is the same either way, bit for
+ * bit: the routing arithmetic is shared and each query block's attention
+ * does not depend on the order the blocks run in.
+ *
+ * solattn_plan_ws: step 2 (page "MiniMax 官宣 NVIDIA Sol 团队 H3 加速:5 秒
+ * 视频 1.653 秒生成并开源", section "提速来自流水线每一段的叠加": block scores,
+ * mean + tau * std threshold, keep mask) for every query block, on a
+ * workspace solattn_prepare_ws filled for the same q, shape, dtype and mode.
+ * Writes into ws each block's keep bits and the number of 64-key tiles its
+ * attention will run, then the dispatch order of the attention launch:
+ * within each (head, XCD) share of the launch, longest first.
+ * solattn_attend_plan_ws: steps 3-5 (exact kept tiles, pooled correction,
+ * one online softmax; page "NVIDIA 团队开源 Sol-H3 的 DGX Spark 版本",
+ * section "119.68 GiB 的内存池") from the plan and tiles in ws into out
+ * ([B][H][N][d] bf16); mode must be the one the plan was made with.  Both
+ * allocate nothing, enqueue kernels on `stream`, and return
+ * SOLATTN_EUNSUPPORTED for fp32, DENSE or SOLATTN_TAYLOR1.
+ */
+int solattn_plan_ws(const void* q, int64_t B, int64_t H, int64_t N, int64_t d,
+                    int64_t prefix_len, float tau, int mode, int dtype, void* ws, size_t ws_bytes,
+                    void* stream);
+int solattn_attend_plan_ws(const void* q, void* out, int64_t B, int64_t H, int64_t N, int64_t d,
+                           int mode, int dtype, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * solattn_forward plus an export of the routing each query block used, from

@@ -94,6 +94,19 @@ def test_other_entry_points_validate(lib):
                         None, None, None) == 1                       # NULL ws
     assert lib.raw_call("solattn_route_ws", A, 1, 1, 64, 64, 0, f(1.0), 1, A, 16, None, None,
                         None, None) == 1                             # too small
+    # the routing plan: bf16 SPARSE / TOPK only, workspace checked on the host
+    plan = lambda mode, dtype, ws=A + 0x1000000, nbytes=1 << 30, tau=1.0: lib.raw_call(
+        "solattn_plan_ws", A, 1, 1, 1024, 64, 0, f(tau), mode, dtype, ws, nbytes, None)
+    attend_plan = lambda mode, dtype, out=A + 0x800000, ws=A + 0x1000000, nbytes=1 << 30: (
+        lib.raw_call("solattn_attend_plan_ws", A, out, 1, 1, 1024, 64, mode, dtype, ws, nbytes,
+                     None))
+    assert plan(1, 1, ws=None) == 1 and plan(1, 1, nbytes=16) == 1
+    assert plan(0, 1) == 2 and plan(1, 0) == 2 and plan(0x41, 1) == 2   # dense, fp32, taylor1
+    assert plan(2, 1, tau=0.0) == 1 and plan(2, 1, tau=2.0) == 1         # topk kept fraction
+    assert plan(1, 1, tau=math.nan) == 1
+    assert attend_plan(0, 1) == 2 and attend_plan(1, 0) == 2 and attend_plan(0x41, 1) == 2
+    assert attend_plan(1, 1, out=None) == 1 and attend_plan(1, 1, ws=None) == 1
+    assert attend_plan(1, 1, out=A) == 1                                 # out overlaps q
 
 
 def test_noalloc_rejects_oversize_shapes_on_host(lib):
