@@ -31,15 +31,17 @@ SEED_LONG = 5000
 # workload: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), scaled by what the
 # same counters read for plain copies of known size in the same runs (x2 for
 # FETCH_SIZE, x1 for WRITE_SIZE).  The figures belong to the kernel sources
-# they were measured on; after any change to those sources the traffic is
-# reported as null until the counters are taken again.
+# they were measured on (the attention kernel and the routing and order
+# kernels, whose dispatch order decides which tiles meet in L2); after any
+# change to those sources the traffic is reported as null until the counters
+# are taken again.
 ATTN_COUNTERS = {
-    "sources_sha256": "b7ea3e6c75cc5e6b8a963e0dd1aed5cb1a1b617a9b239996792d3ae84e799bf6",
-    "fetch_kib": 766616.2, "fetch_scale": 2.0,
-    "write_kib": 131082.6, "write_scale": 1.0,
+    "sources_sha256": "878ec858dcbd9bc226e34c82ee63b6b035af022ba92e935abc8a333707267ec2",
+    "fetch_kib": 334255.8, "fetch_scale": 2.0,
+    "write_kib": 131072.2, "write_scale": 1.0,
     "profile": "profiles/attn_bf16_refine_tau1.25_counters.txt",
 }
-ATTN_SOURCES = ("attn_bf16.hip", "route.h", "common.h", "launch.h", "taylor.h")
+ATTN_SOURCES = ("attn_bf16.hip", "route.h", "route.hip", "common.h", "launch.h", "taylor.h")
 
 
 def attn_sources_sha256():
