@@ -88,12 +88,16 @@ __global__ __launch_bounds__(64 * kRouteG) void route_kernel(AttnArgs a) {
 // units take positions in order as they free up, so its last dispatch round
 // holds its shortest items instead of whichever items the sequence put last.
 // Items of one head stay together, so the head's key/value tiles stay shared
-// in that XCD's L2.  One workgroup ranks 256 items of one head against the
+// in that XCD's L2.  With dense prefix rows the range's prefix query blocks
+// (every key block exact, several times a routed block's tiles) come first,
+// in head order, ahead of every head's routed blocks, as in the fused
+// launch's order.  One workgroup ranks 256 items of one head against the
 // head's counts in LDS.
 __global__ __launch_bounds__(256) void order_kernel(AttnArgs a) {
     extern __shared__ int32_t cnt[];
     // (B*H*Nb < 2^31 is checked on the host: 32-bit indices)
     const int Nb = (int)a.Nb, T = (int)(a.BH * a.Nb);
+    const int Pb = (a.prefix_rows && a.Pb < a.Nb) ? (int)a.Pb : 0;  // heavy items: e < Pb
     const int chunks = (Nb + 255) / 256;
     const int bh = (int)blockIdx.x / chunks, h0 = bh * Nb;
     for (int e = threadIdx.x; e < Nb; e += 256) cnt[e] = a.plan_cost[h0 + e];
@@ -107,16 +111,27 @@ __global__ __launch_bounds__(256) void order_kernel(AttnArgs a) {
     const int x_lo = x * q + (x < m ? x : m), x_hi = x_lo + q + (x < m ? 1 : 0);
     const int lo = (x_lo > h0 ? x_lo : h0) - h0;
     const int hi = (x_hi < h0 + Nb ? x_hi : h0 + Nb) - h0;
-    const int32_t c = cnt[e];
-    int rank = 0;
-    // (every lane reads the same count at once: LDS broadcasts; unrolled so
-    // that several reads are in flight)
+    // heavy items among the first n items of the launch, and in this range
+    auto heavy_before = [&](int n) { return n / Nb * Pb + (n % Nb < Pb ? n % Nb : Pb); };
+    const int hx = heavy_before(x_hi) - heavy_before(x_lo);
+    int pos;
+    if (e < Pb) {
+        pos = x_lo + heavy_before(g) - heavy_before(x_lo);
+    } else {
+        // after the range's heavy items and the other items of earlier heads
+        // in the range, by decreasing count within the head
+        const int s0 = h0 + lo;
+        pos = x_lo + hx + (s0 - x_lo) - (heavy_before(s0) - heavy_before(x_lo));
+        const int32_t c = cnt[e];
+        // (every lane reads the same count at once: LDS broadcasts; unrolled
+        // so that several reads are in flight)
 #pragma unroll 8
-    for (int f = lo; f < hi; ++f) {
-        const int32_t cf = cnt[f];
-        rank += (cf > c) | ((cf == c) & (f < e));
+        for (int f = lo; f < hi; ++f) {
+            const int32_t cf = cnt[f];
+            pos += (f >= Pb) & ((cf > c) | ((cf == c) & (f < e)));
+        }
     }
-    a.plan_perm[h0 + lo + rank] = g;
+    a.plan_perm[pos] = g;
 }
 
 hipError_t launch_order(const AttnArgs& a, hipStream_t s) {
