@@ -36,9 +36,9 @@ SEED_LONG = 5000
 # change to those sources the traffic is reported as null until the counters
 # are taken again.
 ATTN_COUNTERS = {
-    "sources_sha256": "878ec858dcbd9bc226e34c82ee63b6b035af022ba92e935abc8a333707267ec2",
-    "fetch_kib": 334255.8, "fetch_scale": 2.0,
-    "write_kib": 131072.2, "write_scale": 1.0,
+    "sources_sha256": "6a4515b81c77cc7886f3acc014bd097e12df5e94be7505d7e4c8197468971640",
+    "fetch_kib": 334458.9, "fetch_scale": 2.0,
+    "write_kib": 131072.8, "write_scale": 1.0,
     "profile": "profiles/attn_bf16_refine_tau1.25_counters.txt",
 }
 ATTN_SOURCES = ("attn_bf16.hip", "route.h", "route.hip", "common.h", "launch.h", "taylor.h")
