@@ -47,10 +47,15 @@
 //     numerator and denominator agree;
 //   * the routing prologue issues the query block's Q loads between its
 //     score pass and its keep-mask pass, so they arrive under the latter;
+//     in a planned launch (large launches: the routing kernel and the order
+//     kernel ran first) the wave instead takes its query block from the
+//     longest-first dispatch order and rebuilds the same lists from the
+//     block's keep bits, requested ahead of the Q loads;
 //     the epilogue writes each output row with 16-byte stores after a
 //     v_permlane32_swap between the lane halves;
 //   * workgroups are remapped so that the query blocks of one head run on
-//     one XCD and share its L2 for the K/V tiles they keep.
+//     one XCD and share its L2 for the K/V tiles they keep (in a planned
+//     launch, within that XCD's range, longest first).
 // The file also holds attn_bf16_taylor_kernel, the first-order (Taylor)
 // accuracy mode: the same routing, the rescaling path over the exact and
 // pooled tiles, then a pass over every skipped block (see
