@@ -36,8 +36,8 @@ SEED_LONG = 5000
 # change to those sources the traffic is reported as null until the counters
 # are taken again.
 ATTN_COUNTERS = {
-    "sources_sha256": "6a4515b81c77cc7886f3acc014bd097e12df5e94be7505d7e4c8197468971640",
-    "fetch_kib": 334458.9, "fetch_scale": 2.0,
+    "sources_sha256": "f4b74dd34d96411ea15f5b8cb5d2728d209d3d8c74311649dc544336e817327c",
+    "fetch_kib": 334870.2, "fetch_scale": 2.0,
     "write_kib": 131072.8, "write_scale": 1.0,
     "profile": "profiles/attn_bf16_refine_tau1.25_counters.txt",
 }
