@@ -92,18 +92,22 @@ __global__ __launch_bounds__(64 * kRouteG) void route_kernel(AttnArgs a) {
 // (every key block exact, several times a routed block's tiles) come first,
 // in head order, ahead of every head's routed blocks, as in the fused
 // launch's order.  One workgroup ranks 256 items of one head against the
-// head's counts in LDS.
-__global__ __launch_bounds__(256) void order_kernel(AttnArgs a) {
-    extern __shared__ int32_t cnt[];
+// head's counts in LDS; four threads share each item's comparisons, a
+// quarter of its range each, and their counts are added in LDS.
+constexpr int kOrderItems = 256, kOrderParts = 4;
+
+__global__ __launch_bounds__(kOrderItems * kOrderParts) void order_kernel(AttnArgs a) {
+    extern __shared__ int32_t cnt[];  // counts [Nb] | partial ranks [parts][items]
     // (B*H*Nb < 2^31 is checked on the host: 32-bit indices)
     const int Nb = (int)a.Nb, T = (int)(a.BH * a.Nb);
     const int Pb = (a.prefix_rows && a.Pb < a.Nb) ? (int)a.Pb : 0;  // heavy items: e < Pb
-    const int chunks = (Nb + 255) / 256;
+    const int chunks = (Nb + kOrderItems - 1) / kOrderItems;
     const int bh = (int)blockIdx.x / chunks, h0 = bh * Nb;
-    for (int e = threadIdx.x; e < Nb; e += 256) cnt[e] = a.plan_cost[h0 + e];
+    for (int e = threadIdx.x; e < Nb; e += kOrderItems * kOrderParts) cnt[e] = a.plan_cost[h0 + e];
     __syncthreads();
-    const int e = ((int)blockIdx.x % chunks) * 256 + (int)threadIdx.x;
-    if (e >= Nb) return;
+    const int item = (int)threadIdx.x % kOrderItems, part = (int)threadIdx.x / kOrderItems;
+    const int e = ((int)blockIdx.x % chunks) * kOrderItems + item;
+    const bool valid = e < Nb;
     // the XCD range holding position h0 + e (xcd_remap: 8 ranges, the first
     // T % 8 of them one position longer), clipped to this head
     const int g = h0 + e, q = T / 8, m = T % 8;
@@ -111,6 +115,25 @@ __global__ __launch_bounds__(256) void order_kernel(AttnArgs a) {
     const int x_lo = x * q + (x < m ? x : m), x_hi = x_lo + q + (x < m ? 1 : 0);
     const int lo = (x_lo > h0 ? x_lo : h0) - h0;
     const int hi = (x_hi < h0 + Nb ? x_hi : h0 + Nb) - h0;
+    // items of the range ahead of e: by decreasing count within the head,
+    // this thread's quarter [f0, f1) of [lo, hi)
+    int ahead = 0;
+    if (valid && e >= Pb) {
+        const int32_t c = cnt[e];
+        const int f0 = lo + (hi - lo) * part / kOrderParts;
+        const int f1 = lo + (hi - lo) * (part + 1) / kOrderParts;
+        // (the lanes of a wave read the same count at once: LDS broadcasts;
+        // unrolled so that several reads are in flight)
+#pragma unroll 8
+        for (int f = f0; f < f1; ++f) {
+            const int32_t cf = cnt[f];
+            ahead += (f >= Pb) & ((cf > c) | ((cf == c) & (f < e)));
+        }
+    }
+    int32_t* pr = cnt + Nb;
+    pr[part * kOrderItems + item] = ahead;
+    __syncthreads();
+    if (!valid || part != 0) return;
     // heavy items among the first n items of the launch, and in this range
     auto heavy_before = [&](int n) { return n / Nb * Pb + (n % Nb < Pb ? n % Nb : Pb); };
     const int hx = heavy_before(x_hi) - heavy_before(x_lo);
@@ -119,31 +142,25 @@ __global__ __launch_bounds__(256) void order_kernel(AttnArgs a) {
         pos = x_lo + heavy_before(g) - heavy_before(x_lo);
     } else {
         // after the range's heavy items and the other items of earlier heads
-        // in the range, by decreasing count within the head
+        // in the range
         const int s0 = h0 + lo;
         pos = x_lo + hx + (s0 - x_lo) - (heavy_before(s0) - heavy_before(x_lo));
-        const int32_t c = cnt[e];
-        // (every lane reads the same count at once: LDS broadcasts; unrolled
-        // so that several reads are in flight)
-#pragma unroll 8
-        for (int f = lo; f < hi; ++f) {
-            const int32_t cf = cnt[f];
-            pos += (f >= Pb) & ((cf > c) | ((cf == c) & (f < e)));
-        }
+#pragma unroll
+        for (int u = 0; u < kOrderParts; ++u) pos += pr[u * kOrderItems + item];
     }
     a.plan_perm[pos] = g;
 }
 
 hipError_t launch_order(const AttnArgs& a, hipStream_t s) {
-    const size_t lds = sizeof(int32_t) * a.Nb;
-    const dim3 grid((unsigned)(a.BH * ((a.Nb + 255) / 256)));
+    const size_t lds = sizeof(int32_t) * (a.Nb + kOrderItems * kOrderParts);
+    const dim3 grid((unsigned)(a.BH * ((a.Nb + kOrderItems - 1) / kOrderItems)));
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&order_kernel),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(order_kernel, grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL(order_kernel, grid, dim3(kOrderItems * kOrderParts), lds, s, a);
     return hipGetLastError();
 }
 
