@@ -466,7 +466,9 @@ __device__ inline void produce_rows(const T* __restrict__ base, T* __restrict__ 
     for (int p = 0; p < PASSES; ++p) {
         const int r = r0 + p * RPP;
         if (r < n) {
-            xs[p] = *reinterpret_cast<const typename Vec16<T>::type*>(base + (int64_t)r * D + c * VEC);
+            // (non-temporal, as in load_rows: each pre-norm row is read once)
+            xs[p] = __builtin_nontemporal_load(
+                reinterpret_cast<const typename Vec16<T>::type*>(base + (int64_t)r * D + c * VEC));
         } else {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) xs[p][e] = (T)0.f;
