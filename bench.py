@@ -36,9 +36,9 @@ SEED_LONG = 5000
 # change to those sources the traffic is reported as null until the counters
 # are taken again.
 ATTN_COUNTERS = {
-    "sources_sha256": "f4b74dd34d96411ea15f5b8cb5d2728d209d3d8c74311649dc544336e817327c",
-    "fetch_kib": 334870.2, "fetch_scale": 2.0,
-    "write_kib": 131072.8, "write_scale": 1.0,
+    "sources_sha256": "ddc6eaab6dce9c4d91dfd71778395714773525da334ba3768ea8c6f6cde283d8",
+    "fetch_kib": 334214.7, "fetch_scale": 2.0,
+    "write_kib": 131073.3, "write_scale": 1.0,
     "profile": "profiles/attn_bf16_refine_tau1.25_counters.txt",
 }
 ATTN_SOURCES = ("attn_bf16.hip", "route.h", "route.hip", "common.h", "launch.h", "taylor.h")
