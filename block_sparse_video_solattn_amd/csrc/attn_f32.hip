@@ -47,11 +47,17 @@ __global__ __launch_bounds__(64 * kF32Waves) void attn_f32_kernel(AttnArgs a) {
 
     // Every wave routes the block into its own LDS slice (the same code on
     // the same values: identical lists; every wave reaches the routing's
-    // barriers).
+    // barriers); only wave 0 writes the debug exports.
+    AttnArgs ar = a;
+    if (__builtin_amdgcn_readfirstlane(wave) != 0) {
+        ar.mask_out = nullptr;
+        ar.score_out = nullptr;
+        ar.thr_out = nullptr;
+    }
     int n_kept;
     uint64_t tile_mask;
     if (a.mode != kDense) {
-        const RouteResult r = route_query_block<D>(a, bh, i, srow, klist);
+        const RouteResult r = route_query_block<D>(ar, bh, i, srow, klist);
         n_kept = r.n_kept;
         tile_mask = r.tile_mask;
     } else {
